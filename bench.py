@@ -1,0 +1,207 @@
+"""Decode-step benchmark: split-KV decode attention at a 1M-token context on
+one MI355X.
+
+One step = kv_append of the newest token of every (request, KV head) +
+decode_attn_partial over all slices + lse_combine, on one stream, with the
+cache already resident in HBM.  Inputs are synthetic (seeded), shaped like
+the named workload.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from long_context_decode_split_amd import api, configs, roofline, synth
+
+DEFAULT_WORKLOAD = configs.LLAMA405B_SHARE.name
+METRIC = "µs/layer/decode step and KV-read HBM GB/s (% of peak) at 1M-token context"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def setup(w, seed):
+    t0 = time.time()
+    inp = synth.make_inputs(w, seed, device="cuda")
+    desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=w.v_alias_k, dtype=w.dtype, cap=inp.cap)
+    cache = api.KVCache(desc, device="cuda")
+    # the cache holds n-1 tokens of every request before the step
+    api.kv_append(cache, inp.k, inp.v, inp.k_scale, inp.v_scale, pos=[0] * w.B, count=[n - 1 for n in inp.ctx])
+    last = [n - 1 for n in inp.ctx]
+
+    def newest(t):
+        if t is None:
+            return None
+        return torch.stack([t[b, :, last[b]:last[b] + 1] for b in range(w.B)]).contiguous()
+
+    step_in = dict(k=newest(inp.k), v=newest(inp.v), ks=newest(inp.k_scale), vs=newest(inp.v_scale), pos=last)
+    ws = torch.zeros(api.workspace_size(desc, w.Hq), dtype=torch.uint8, device="cuda")
+    o_part = torch.empty(w.P, w.B, w.Hq, w.Dv, dtype=torch.float32, device="cuda")
+    lse_part = torch.empty(w.P, w.B, w.Hq, dtype=torch.float32, device="cuda")
+    o = torch.empty(w.B, w.Hq, w.Dv, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] setup {w.name}: ctx={inp.ctx[:4]}{'...' if w.B > 4 else ''} cap={inp.cap} "
+        f"cache={cache.nbytes() / 1e9:.3f} GB in {time.time() - t0:.1f}s")
+    return inp, cache, step_in, ws, o_part, lse_part, o, lse
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    """The oracle (fp64, numpy) on a bounded sample of the same step: whole
+    (request, KV head) groups over their full context, as many as fit the
+    time budget (at least one); scaled to KV-read GB/s like the GPU value."""
+    from oracle import attention as oatt
+    from oracle import codecs as ocod
+
+    w = inp.w
+    G = w.G
+    per_tok = roofline.kv_bytes_per_token(w.Dk, w.Dv, w.v_alias_k, w.dtype)
+    done_bytes, t_total, groups = 0.0, 0.0, 0
+    order = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    for b, g in order:
+        n = inp.ctx[b]
+        # host copies of the generator's storage-format tensors (not timed)
+        kc = inp.k[b, g, :n].cpu()
+        vc = None if inp.v is None else inp.v[b, g, :n].cpu()
+        ks = None if inp.k_scale is None else inp.k_scale[b, g, :n].cpu().numpy()
+        vs = None if inp.v_scale is None else inp.v_scale[b, g, :n].cpu().numpy()
+        q = ocod.bf16_bits_to_f64(inp.q[b, g * G:(g + 1) * G].cpu().view(torch.int16).numpy().view(np.uint16))
+        t0 = time.perf_counter()
+        if w.dtype == "bf16":
+            K = ocod.bf16_bits_to_f64(kc.view(torch.int16).numpy().view(np.uint16))
+            V = K[:, :w.Dv] if w.v_alias_k else ocod.bf16_bits_to_f64(vc.view(torch.int16).numpy().view(np.uint16))
+        elif w.dtype == "fp8_e4m3":
+            K = ocod.dequant_fp8(kc.numpy(), ks[::16])
+            V = K[:, :w.Dv] if w.v_alias_k else ocod.dequant_fp8(vc.numpy(), vs[::16])
+        else:
+            K = ocod.dequant_mxfp4(kc.numpy(), ks)
+            V = K[:, :w.Dv] if w.v_alias_k else ocod.dequant_mxfp4(vc.numpy(), vs)
+        oatt.attend(q, K, V, w.softmax_scale)
+        t_total += time.perf_counter() - t0
+        done_bytes += n * per_tok
+        groups += 1
+        del K, V
+        if t_total >= budget_s:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {
+        "value": done_bytes / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{groups} of {len(order)} (request, KV head) groups of the same step, full context each; "
+                  f"fp64 numpy unsplit attention incl. decoding the stored K/V; {t_total:.1f}s",
+        "us_per_layer_step_extrapolated": t_total / done_bytes * roofline.kv_bytes(w, inp.ctx) * 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(configs.ALL))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the KV-parallel slices of this build are slices of one GPU's HBM, and "
+              "no collectives are built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = configs.ALL[args.workload]
+    inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        api.kv_append(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        api.decode_attn_partial(cache, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        api.lse_combine(o_part, lse_part, o, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(kev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_avg_ms = float(np.mean(kern_ms))
+
+    nbytes = roofline.kv_bytes(w, inp.ctx)
+    flops = roofline.attn_flops(w, inp.ctx)
+    step_gbs = nbytes / (step_ms * 1e-3) / 1e9
+    kern_gbs = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    peak_gbs = roofline.HBM_PEAK_BYTES_PER_S / 1e9
+    log(f"[bench] step {step_ms * 1e3:.1f} us, partial kernel {kern_avg_ms * 1e3:.1f} us "
+        f"(min {min(kern_ms) * 1e3:.1f}, max {max(kern_ms) * 1e3:.1f}), {kern_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "us_per_layer_step": round(step_ms * 1e3, 2),
+        "frac_of_hbm_peak": round(step_gbs / peak_gbs, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3 KV, bf16 MFMA, fp32 acc",
+                  "mxfp4": "mxfp4 KV, bf16 MFMA, fp32 acc"}[w.dtype] if w.dtype != "bf16" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "Dk": w.Dk, "Dv": w.Dv,
+            "v_alias_k": w.v_alias_k, "kv_dtype": w.dtype, "slices": w.P,
+            "context": inp.ctx if w.ctx is None else w.ctx, "kv_bytes_per_step": nbytes, "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_attn_partial",
+            "achieved": round(kern_gbs, 2),
+            "peak": peak_gbs,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / peak_gbs, 4),
+            "traffic": None,
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
+            "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

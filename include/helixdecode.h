@@ -1,0 +1,202 @@
+/*
+ * helixdecode — KV-parallel (sequence-split) decode attention for one
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (the method's data-parallel hot path):
+ *   "Helix Parallelism: Rethinking Sharding Strategies for Interactive
+ *   Multi-Million-Token LLM Decoding" (fdeinterviews.com summary), paragraph
+ *   on KV parallelism: the request's KV history is split along the sequence;
+ *   every slice attends over its part and returns a partial output and a
+ *   log-sum-exp; one exchange then combines the partials into the exact
+ *   attention output.  Same page, paragraph on Helix's two layouts: new KV
+ *   entries rotate across the slices every 16 tokens.  jaehun.me review,
+ *   Prompt 1.3.2 "The Secret Weapon": the combine is
+ *   O = sum_i O_i exp(LSE_i) / sum_i exp(LSE_i), exact.
+ *
+ * On one GPU every KV-parallel rank becomes one slice of an HBM-resident
+ * cache, and the exchange becomes an in-HBM combine (hx_lse_combine).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every function returns an hx_status; HX_OK is 0.  Arguments are checked
+ *    on the host before anything is launched; on error nothing is launched
+ *    and hx_last_error() returns a message (thread-local, valid until the
+ *    next call on the same thread).  Nothing throws across the ABI.
+ *  - Pointers named "device" are device memory owned by the caller; the
+ *    library never allocates, frees or keeps them.  Pointers named "host"
+ *    are read before the call returns.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *    work is asynchronous and ordered on that stream only; the call does not
+ *    synchronise.
+ *  - Device pointers must be 16-byte aligned (HX_EINVAL otherwise).
+ *  - HX_EHIP reports a HIP runtime error from the launch (e.g. no device).
+ *
+ * Layout words used below: B requests, Hkv KV heads, Hq query heads,
+ * G = Hq / Hkv query heads per KV head, Dk / Dv key and value widths,
+ * P slices, cap rows per slice plane (a multiple of 16).
+ */
+#ifndef HELIXDECODE_H
+#define HELIXDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HX_OK = 0,
+  HX_EINVAL = 1,       /* bad argument (null, misaligned, out of range) */
+  HX_EUNSUPPORTED = 2, /* valid but not implemented (shape / dtype combo) */
+  HX_EHIP = 3          /* the HIP runtime reported an error */
+} hx_status;
+
+typedef enum {
+  HX_KV_BF16 = 0,     /* bf16 K and V */
+  HX_KV_FP8_E4M3 = 1, /* OCP fp8 e4m3 codes, one fp32 scale per 16-row group */
+  HX_KV_MXFP4 = 2     /* OCP MX FP4 (e2m1) codes, one e8m0 scale per 32 elements of a row */
+} hx_kv_dtype;
+
+/* Token-group size of the placement: the unit that rotates over slices. */
+#define HX_CHUNK 16
+
+/* Describes one KV cache (one layer).  Supported combinations:
+ *   GQA: Dk = Dv = 128, v_alias_k = 0, dtype any, 1 <= G <= 16;
+ *   MLA: Dk = 576, Dv = 512, v_alias_k = 1 (V is the first 512 columns of
+ *        the K row: one latent KV head), dtype HX_KV_BF16, G = 128.
+ * Other combinations return HX_EUNSUPPORTED. */
+typedef struct {
+  int32_t P;          /* slices (KV-parallel ranks), 1..64 */
+  int32_t B;          /* requests, >= 1 */
+  int32_t Hkv;        /* KV heads, >= 1 */
+  int32_t Dk;         /* key width */
+  int32_t Dv;         /* value width */
+  int32_t v_alias_k;  /* 1: V = K[..., :Dv]; the V plane is absent */
+  int32_t dtype;      /* hx_kv_dtype */
+  int32_t reserved;   /* must be 0 */
+  int64_t cap;        /* rows per slice plane, a positive multiple of 16 */
+} hx_kv_desc;
+
+/* Device pointers of the cache planes (all caller-owned):
+ *   k, v      : codes, [P][B][Hkv][cap/16] chunk tiles of 16 rows each.  The
+ *               byte order inside a tile is the library's (chosen so the
+ *               attention kernels load matrix-core operands with 1 KiB
+ *               coalesced reads); hx_kv_tile_offset() documents it.  Write
+ *               with hx_kv_append, read rows back with hx_kv_dequant.
+ *   k_scale,  : HX_KV_FP8_E4M3: float [P][B][Hkv][cap/16] (one per tile);
+ *   v_scale     HX_KV_MXFP4: uint8 e8m0 [P][B][Hkv][cap][D/32] (row-major);
+ *               HX_KV_BF16: unused (NULL).
+ * v and v_scale are NULL when v_alias_k = 1. */
+typedef struct {
+  void* k;
+  void* v;
+  void* k_scale;
+  void* v_scale;
+} hx_kv_cache;
+
+/* Byte sizes the caller allocates for each plane, and the tile sizes. */
+typedef struct {
+  size_t k_bytes, v_bytes, k_scale_bytes, v_scale_bytes;
+  size_t k_tile_bytes, v_tile_bytes; /* bytes of one 16-row chunk tile */
+  int64_t n_max;                     /* largest context: P * cap */
+} hx_kv_layout_info;
+
+/* Thread-local message of the last failing call ("" if none). */
+const char* hx_last_error(void);
+
+/* Library version string. */
+const char* hx_version(void);
+
+/* Sizes of the cache planes for `desc`.  Host only; no device work. */
+hx_status hx_kv_layout(const hx_kv_desc* desc, hx_kv_layout_info* out);
+
+/* Placement (host only).  Token t (0-based, per request) belongs to the
+ * 16-token group t / 16; groups are dealt to the P slices in turn starting
+ * at slice 0, so *r = (t / 16) mod P and the local row is
+ * *j = ((t / 16) / P) * 16 + t mod 16 (rows keep arrival order).
+ * Sources: Helix summary, paragraph on Helix's two layouts (rotation every
+ * 16 tokens); NVIDIA technical blog (open-lab.net, Korean), section on
+ * distributed KV placement (tokens 1-16 on rank 0, 17-32 on rank 1). */
+hx_status hx_slot(int64_t t, int32_t P, int32_t* r, int64_t* j);
+
+/* Rows held by slice r when a request has n tokens (host only):
+ * floor(n / 16P) * 16 + clamp(n - floor(n / 16P) * 16P - 16 r, 0, 16). */
+hx_status hx_slice_len(int64_t n, int32_t P, int32_t r, int64_t* len);
+
+/* Byte offset (times 2, plus 1 for the high nibble of an FP4 code) of
+ * element (row m of the tile, column d) inside a chunk tile of the K
+ * (which = 0) or V (which = 1) plane.  Host only; documents the tile
+ * layout for callers that write tiles themselves. */
+hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, int32_t d, int64_t* off2);
+
+/* Append new tokens for every KV head, placing each by hx_slot: request b
+ * gets count[b] consecutive tokens (count = NULL: n_new each, count[b] may
+ * be 0) starting at token pos[b] (pos, count: host arrays [B]).
+ * Inputs are device arrays in storage format, token-major, with n_new rows
+ * per (request, head), of which request b uses the first count[b]:
+ *   k_new [B][Hkv][n_new][Dk], v_new [B][Hkv][n_new][Dv] (v_new NULL if
+ *   v_alias_k): bf16 -> 2 bytes per element; fp8 -> 1 byte; MXFP4 -> packed
+ *   bytes [..][Dk/2], even element in the low nibble;
+ *   k_scale_new / v_scale_new: fp8 -> float [B][Hkv][n_new], the scale of
+ *   the 16-token group each token falls in (the group's stored scale is
+ *   taken from the first new token of that group in this call; every token
+ *   of a group must carry the same scale, since earlier codes of a group
+ *   keep the stored scale); MXFP4 -> uint8 e8m0 [B][Hkv][n_new][D/32];
+ *   bf16 -> NULL.
+ * Pure placement: the bytes are copied, never converted, so it is
+ * bit-exact.  Rows outside [pos[b], pos[b] + count[b]) are left unchanged.
+ * Requires n_new >= 1, 0 <= count[b] <= n_new, 0 <= pos[b] and
+ * pos[b] + count[b] <= P * cap. */
+hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                       const void* k_scale_new, const void* v_scale_new, const int64_t* pos, const int32_t* count,
+                       int32_t n_new, void* stream);
+
+/* Decode rows [j0, j0 + n) of slice r, request b, KV head g into fp32:
+ * k_out [n][Dk], v_out [n][Dv] (device; v_out may be NULL).  bf16: exact
+ * widening; fp8: fp32 product code * scale rounded to nearest-even; MXFP4:
+ * code * 2^(E-127), exact.  For tests and inspection, not the hot path. */
+hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
+                        int64_t j0, int64_t n, float* k_out, float* v_out, void* stream);
+
+/* Workspace bytes hx_decode_attn_partial needs for `desc` with Hq query
+ * heads (host only).  The workspace must be zero-filled before its first
+ * use (hx_workspace_init does that); every call leaves its counters at zero
+ * again, so one workspace serves any number of calls on one stream. */
+hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes);
+
+/* Zero a workspace (device) on `stream`. */
+hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Per-slice partial attention for one decode step, every slice in one
+ * launch (Helix summary, paragraph on KV parallelism: each slice attends
+ * over its part of the history and returns a partial output and a
+ * log-sum-exp).
+ *   q        device bf16 [B][Hq][Dk]; query head h uses KV head h / G.
+ *   ctx_len  host int64 [B]: tokens of request b, 1 <= ctx_len[b] <= P*cap;
+ *            slice r holds hx_slice_len(ctx_len[b], P, r) rows.
+ *   scale    softmax scale applied to q.k (e.g. 1/sqrt(Dk)).
+ *   o_part   device float [P][B][Hq][Dv]: O_r = sum_t softmax_r(s)_t V_t
+ *            over slice r's tokens (normalised); 0 for an empty slice.
+ *   lse_part device float [P][B][Hq]: LSE_r = ln sum_{t in r} exp(s_t)
+ *            (natural log); -inf for an empty slice.
+ *   ws       device workspace of hx_workspace_size bytes (see there).
+ * Calls that share a workspace must be ordered (same stream). */
+hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                                 const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* LSE-weighted combine of P partials (jaehun.me review, Prompt 1.3.2):
+ *   m = max_r LSE_r, w_r = exp(LSE_r - m),
+ *   o = sum_r w_r O_r / sum_r w_r,  lse = m + ln sum_r w_r.
+ * o_part [P][B][Hq][Dv], lse_part [P][B][Hq] (device float) ->
+ * o [B][Hq][Dv], lse [B][Hq] (device float).  All-empty rows (every
+ * LSE_r = -inf) give o = 0, lse = -inf.  1 <= P <= 1024. */
+hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,
+                         float* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HELIXDECODE_H */

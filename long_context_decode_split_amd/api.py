@@ -1,0 +1,157 @@
+"""Thin Python binding of the helixdecode C ABI (include/helixdecode.h).
+
+Every function here only turns torch tensors into pointers and host arrays
+into ctypes arrays, then calls the library entry point of the same name; all
+device work runs in the library's HIP kernels.  Errors raise ``HXError``.
+PyTorch provides device memory and the current stream, nothing else.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import (HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXError, check, hx_kv_cache, hx_kv_desc,
+                   hx_kv_layout_info, lib)
+
+__all__ = ["HXError", "KVDesc", "KVCache", "DTYPES", "kv_layout", "slot", "slice_len", "kv_tile_offset", "kv_append",
+           "kv_dequant", "workspace_size", "workspace_init", "decode_attn_partial", "lse_combine", "version",
+           "exported_symbols"]
+
+DTYPES = {"bf16": HX_KV_BF16, "fp8_e4m3": HX_KV_FP8_E4M3, "mxfp4": HX_KV_MXFP4}
+
+
+@dataclass(frozen=True)
+class KVDesc:
+    """Mirror of ``hx_kv_desc``."""
+    P: int
+    B: int
+    Hkv: int
+    Dk: int
+    Dv: int
+    v_alias_k: bool
+    dtype: str
+    cap: int
+
+    def c(self):
+        return hx_kv_desc(self.P, self.B, self.Hkv, self.Dk, self.Dv, int(self.v_alias_k), DTYPES[self.dtype], 0,
+                          self.cap)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _i64(values):
+    values = [int(v) for v in values]
+    return (ctypes.c_int64 * len(values))(*values)
+
+
+def version():
+    return lib().hx_version().decode()
+
+
+def exported_symbols():
+    from ._lib import SIGNATURES
+    return sorted(SIGNATURES)
+
+
+def kv_layout(desc: KVDesc):
+    info = hx_kv_layout_info()
+    check(lib().hx_kv_layout(ctypes.byref(desc.c()), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in hx_kv_layout_info._fields_}
+
+
+def slot(t, P):
+    r = ctypes.c_int32()
+    j = ctypes.c_int64()
+    check(lib().hx_slot(t, P, ctypes.byref(r), ctypes.byref(j)))
+    return r.value, j.value
+
+
+def slice_len(n, P, r):
+    out = ctypes.c_int64()
+    check(lib().hx_slice_len(n, P, r, ctypes.byref(out)))
+    return out.value
+
+
+def kv_tile_offset(desc: KVDesc, which, m, d):
+    out = ctypes.c_int64()
+    check(lib().hx_kv_tile_offset(ctypes.byref(desc.c()), which, m, d, ctypes.byref(out)))
+    return out.value
+
+
+class KVCache:
+    """The cache planes of one layer, allocated with torch on ``device``
+    using the sizes ``hx_kv_layout`` reports.  ``fill`` sets every byte (use
+    0xFF to make unwritten rows NaN in every format)."""
+
+    def __init__(self, desc: KVDesc, device="cuda", fill=None):
+        self.desc = desc
+        lay = kv_layout(desc)
+        self.layout = lay
+
+        def plane(nbytes):
+            if nbytes == 0:
+                return None
+            t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            return t
+
+        self.k = plane(lay["k_bytes"])
+        self.v = plane(lay["v_bytes"])
+        self.k_scale = plane(lay["k_scale_bytes"])
+        self.v_scale = plane(lay["v_scale_bytes"])
+
+    def c(self):
+        return hx_kv_cache(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale))
+
+    def nbytes(self):
+        return sum(t.numel() for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None)
+
+
+def kv_append(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, pos, count=None, stream=None):
+    """``hx_kv_append``: token-major storage-format tensors of shape
+    [B, Hkv, n_new, ...]; ``pos`` (and ``count``) are host sequences of B ints."""
+    n_new = k_new.shape[2]
+    cnt = None if count is None else (ctypes.c_int32 * len(count))(*[int(c) for c in count])
+    check(lib().hx_kv_append(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+                             _ptr(k_scale_new), _ptr(v_scale_new), _i64(pos), cnt, n_new, _stream(stream)))
+
+
+def kv_dequant(cache: KVCache, r, b, g, j0, n, k_out, v_out=None, stream=None):
+    check(lib().hx_kv_dequant(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), r, b, g, j0, n, _ptr(k_out),
+                              _ptr(v_out), _stream(stream)))
+
+
+def workspace_size(desc: KVDesc, Hq):
+    out = ctypes.c_size_t()
+    check(lib().hx_workspace_size(ctypes.byref(desc.c()), Hq, ctypes.byref(out)))
+    return out.value
+
+
+def workspace_init(ws, stream=None):
+    check(lib().hx_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_attn_partial(cache: KVCache, q, ctx_len, scale, o_part, lse_part, ws, stream=None):
+    """``hx_decode_attn_partial``: q bf16 [B, Hq, Dk] -> o_part f32
+    [P, B, Hq, Dv], lse_part f32 [P, B, Hq]."""
+    Hq = q.shape[1]
+    check(lib().hx_decode_attn_partial(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq,
+                                       _i64(ctx_len), float(scale), _ptr(o_part), _ptr(lse_part), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lse_combine(o_part, lse_part, o, lse, stream=None):
+    """``hx_lse_combine``: o_part [P, B, Hq, Dv], lse_part [P, B, Hq] ->
+    o [B, Hq, Dv], lse [B, Hq] (all float32)."""
+    P, B, Hq, Dv = o_part.shape
+    check(lib().hx_lse_combine(P, B, Hq, Dv, _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), _stream(stream)))

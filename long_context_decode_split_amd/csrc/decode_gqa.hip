@@ -1,0 +1,409 @@
+// Split-KV decode attention for GQA caches (Dk = Dv = 128, up to 16 query
+// heads per KV head) on gfx950.
+//
+// What one launch computes (Helix summary, paragraph on KV parallelism): for
+// every request b, KV head g and slice r, the partial attention of the G
+// query heads of g over the rows of slice r, as a normalised output and a
+// natural-log LSE.  The rows of a slice are cut into splits of `cpw` 16-row
+// chunk tiles so the launch fills the GPU; each workgroup streams one split,
+// and the last workgroup of a slice to finish folds the splits of that slice
+// with the LSE combine (jaehun.me review, Prompt 1.3.2).
+//
+// Work per wave, per 16-row chunk tile (no LDS on the streaming path):
+//   * 4 x 16 B loads of K and 4 x 16 B loads of V (bf16; fewer for fp8 and
+//     MXFP4), each wave-wide load reading 1 KiB contiguous;
+//   * S^T = K Q^T with four v_mfma_f32_16x16x32_bf16 (rows = tokens,
+//     columns = query heads);
+//   * online softmax in base 2 on the accumulator layout: lane l holds the
+//     scores of head l % 16 for tokens 4*(l/16)..+3, so the row max needs two
+//     lane exchanges and the running sum stays per lane;
+//   * O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16, whose B operand is
+//     the probability fragment exactly as the first product left it.
+// The per-head rescale of the accumulator runs only when some head's max grew.
+
+#include "hx_common.h"
+
+namespace hx {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kWaves = kGqaWavesPerWg;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = 128;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ s16x4 as_s16x4(uint32_t lo, uint32_t hi) {
+  uint2 t = make_uint2(lo, hi);
+  return __builtin_bit_cast(s16x4, t);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp8 e4m3 byte pairs -> packed bf16 (exact: e4m3 values are bf16 values).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Two e2m1 codes of byte `sel` -> packed bf16, multiplied by `scale`.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+
+// e8m0 -> fp32 2^(E-127) (E = 0 gives 2^-127, E = 255 gives NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u) : (e == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e << 23));
+}
+
+// Raw bytes of one chunk tile that a lane needs; FMT 0 bf16, 1 fp8, 2 MXFP4.
+template <int FMT>
+struct Frag;
+
+template <>
+struct Frag<0> {
+  uint4 k[4], v[4];
+  __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, const uint8_t*, const uint8_t*, int lane,
+                                       int) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = ld16(kt + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld16(vt + i * 1024 + lane * 16);
+  }
+};
+
+template <>
+struct Frag<1> {
+  uint4 k[2], v[2];
+  float ks, vs;
+  __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, const uint8_t* kst, const uint8_t* vst,
+                                       int lane, int) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) k[i] = ld16(kt + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[i] = ld16(vt + i * 1024 + lane * 16);
+    ks = *reinterpret_cast<const float*>(kst);
+    vs = *reinterpret_cast<const float*>(vst);
+  }
+};
+
+template <>
+struct Frag<2> {
+  uint4 k, v, vsc;
+  uint32_t ksc;
+  __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, const uint8_t* kst, const uint8_t* vst,
+                                       int lane, int) {
+    k = ld16(kt + lane * 16);
+    v = ld16(vt + lane * 16);
+    ksc = *reinterpret_cast<const uint32_t*>(kst + (lane & 15) * 4);    // 4 e8m0 of token m
+    vsc = ld16(vst + (lane >> 4) * 16);                               // tokens 4h..4h+3, 4 blocks each
+  }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = lane & 15;   // head column / token row inside a fragment
+  const int h = lane >> 4;   // lane group
+
+  // ---- which (request, KV head, slice, split) this workgroup owns
+  const int wg = blockIdx.x;
+  int bl = 0;
+  while (bl + 1 < a.nb && a.wg_begin[bl + 1] <= wg) ++bl;
+  const int nsplit = a.nsplit[bl];
+  int rem = wg - a.wg_begin[bl];
+  const int split = rem % nsplit;
+  rem /= nsplit;
+  const int r = rem % a.P;
+  const int g = rem / a.P;
+  const int b = a.b0 + bl;
+
+  const int64_t L = slice_len(a.n[bl], a.P, r);
+  const int nch = (int)((L + kChunk - 1) / kChunk);
+  const int c0 = split * a.cpw;
+  const int c1 = min(c0 + a.cpw, nch);
+  const int tail_valid = (int)(L - (int64_t)(nch - 1) * kChunk);   // rows in the last chunk
+
+  const int64_t tile0 = ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
+  const uint8_t* kp = a.k + tile0 * a.k_tile;
+  const uint8_t* vp = a.v + tile0 * a.v_tile;
+  const uint8_t* ksp = a.ks ? a.ks + tile0 * a.ks_tile : nullptr;
+  const uint8_t* vsp = a.vs ? a.vs + tile0 * a.vs_tile : nullptr;
+
+  // ---- query fragment: B operand of S^T = K Q^T, head m, columns 32s+8h..+7
+  bf16x8 qf[4];
+  {
+    const bool live = m < a.G;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * a.G + (live ? m : 0)) * a.Dk;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 t = *reinterpret_cast<const uint4*>(qrow + s * 32 + h * 8);
+      if (!live) t = make_uint4(0, 0, 0, 0);
+      qf[s] = as_bf16x8(t);
+    }
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY;   // running max of head m, base-2 units; equal on the 4 lanes of a head
+  float lsum = 0.f;         // this lane's share of the running sum
+
+  const float c2 = a.c2;
+  Frag<FMT> nxt;
+  int c = c0 + wave;
+  if (c < c1) nxt.load(kp + (int64_t)c * a.k_tile, vp + (int64_t)c * a.v_tile, ksp ? ksp + (int64_t)c * a.ks_tile : nullptr,
+                       vsp ? vsp + (int64_t)c * a.vs_tile : nullptr, lane, 0);
+  for (; c < c1; c += kWaves) {
+    Frag<FMT> cur = nxt;
+    const int cn = c + kWaves;
+    if (cn < c1)
+      nxt.load(kp + (int64_t)cn * a.k_tile, vp + (int64_t)cn * a.v_tile, ksp ? ksp + (int64_t)cn * a.ks_tile : nullptr,
+               vsp ? vsp + (int64_t)cn * a.vs_tile : nullptr, lane, 0);
+
+    // ---- K fragments as bf16
+    bf16x8 kf[4];
+    float cscale = c2;
+    if constexpr (FMT == 0) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
+    } else if constexpr (FMT == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t w[4] = {cur.k[i].x, cur.k[i].y, cur.k[i].z, cur.k[i].w};
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {   // bytes 0-7 -> step 2i, 8-15 -> step 2i+1
+          uint4 t;
+          t.x = fp8x2_to_bf16x2<false>(w[2 * hs]);
+          t.y = fp8x2_to_bf16x2<true>(w[2 * hs]);
+          t.z = fp8x2_to_bf16x2<false>(w[2 * hs + 1]);
+          t.w = fp8x2_to_bf16x2<true>(w[2 * hs + 1]);
+          kf[2 * i + hs] = as_bf16x8(t);
+        }
+      }
+      cscale = c2 * cur.ks;
+    } else {
+      const uint32_t w[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float sc = e8m0_to_f32((cur.ksc >> (8 * s)) & 0xff);
+        uint4 t;
+        t.x = fp4x2_to_bf16x2<0>(w[s], sc);
+        t.y = fp4x2_to_bf16x2<1>(w[s], sc);
+        t.z = fp4x2_to_bf16x2<2>(w[s], sc);
+        t.w = fp4x2_to_bf16x2<3>(w[s], sc);
+        kf[s] = as_bf16x8(t);
+      }
+    }
+
+    // ---- scores: S^T[token 4h+i][head m]
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
+
+    const bool tail = (c == nch - 1) && (tail_valid < kChunk);
+    uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;   // V halves of tokens 4h+{0,1} / 4h+{2,3}
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * h + i >= tail_valid) sc[i] = -INFINITY;
+      keep01 = (4 * h + 0 < tail_valid ? 0x0000ffffu : 0u) | (4 * h + 1 < tail_valid ? 0xffff0000u : 0u);
+      keep23 = (4 * h + 2 < tail_valid ? 0x0000ffffu : 0u) | (4 * h + 3 < tail_valid ? 0xffff0000u : 0u);
+    }
+
+    // ---- online softmax (base 2)
+    float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    const float mnew = fmaxf(mrun, cm * cscale);
+    if (__builtin_amdgcn_ballot_w64(mnew > mrun)) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      lsum *= alpha;
+      mrun = mnew;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -mrun));
+
+    // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
+    if constexpr (FMT == 0) {
+      const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+      lsum += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
+      const s16x4 pb = as_s16x4(p01, p23);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 vv = cur.v[i];
+        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.x & keep01, vv.y & keep23), pb, acc[2 * i], 0, 0, 0);
+        acc[2 * i + 1] =
+            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.z & keep01, vv.w & keep23), pb, acc[2 * i + 1], 0, 0, 0);
+      }
+    } else if constexpr (FMT == 1) {
+      // V scale of the tile folded into P; the sum uses the rounded values.
+      const float vsc = cur.vs;
+      const uint32_t p01 = pack_bf16(p[0] * vsc, p[1] * vsc), p23 = pack_bf16(p[2] * vsc, p[3] * vsc);
+      lsum += ((bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23))) * (1.0f / vsc);
+      const s16x4 pb = as_s16x4(p01, p23);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t w[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // column block nb = 4i + q: 4 codes (tokens 4h..4h+3)
+          const uint32_t lo = fp8x2_to_bf16x2<false>(w[q]) & keep01;
+          const uint32_t hi = fp8x2_to_bf16x2<true>(w[q]) & keep23;
+          acc[4 * i + q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo, hi), pb, acc[4 * i + q], 0, 0, 0);
+        }
+      }
+    } else {
+      // Per (token, 32-column block) scales are powers of two: fold them into
+      // P (exact), one P fragment per block; the sum uses unscaled rounded P.
+      const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+      lsum += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
+      const float pr[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
+      const uint32_t vs[4] = {cur.vsc.x, cur.vsc.y, cur.vsc.z, cur.vsc.w};   // token 4h+j: 4 block scales
+      const uint32_t w[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float ps[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ps[j] = pr[j] * e8m0_to_f32((vs[j] >> (8 * blk)) & 0xff);
+        if (tail) {   // rows past the slice end may hold any scale byte, NaN included
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * h + j >= tail_valid) ps[j] = 0.f;
+        }
+        const s16x4 pb = as_s16x4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]));
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int nb = 2 * blk + hb;   // bytes 2nb, 2nb+1 of the lane's 16 B
+          const uint32_t word = w[nb >> 1];
+          uint32_t lo, hi;
+          if ((nb & 1) == 0) {
+            lo = fp4x2_to_bf16x2<0>(word, 1.0f);
+            hi = fp4x2_to_bf16x2<1>(word, 1.0f);
+          } else {
+            lo = fp4x2_to_bf16x2<2>(word, 1.0f);
+            hi = fp4x2_to_bf16x2<3>(word, 1.0f);
+          }
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo & keep01, hi & keep23), pb, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- fold the lanes' running sums of each head
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // ---- combine the waves of this workgroup (LSE rule, base 2)
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_acc[kWaves][16][kD + 4];
+  if (h == 0) {
+    s_m[wave][m] = mrun;
+    s_l[wave][m] = lsum;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    *reinterpret_cast<f32x4*>(&s_acc[wave][m][16 * nb + 4 * h]) = acc[nb];
+  __syncthreads();
+
+  const int G = a.G;
+  const bool direct = nsplit == 1;
+  float* out_o;
+  float* out_l;
+  int64_t ostride_head;   // floats between heads in the output
+  if (direct) {
+    out_o = a.o_part + (((int64_t)r * a.Btot + b) * a.Hq + g * G) * a.Dv;
+    out_l = a.lse_part + ((int64_t)r * a.Btot + b) * a.Hq + g * G;
+  } else {
+    out_o = a.ws_o + (int64_t)wg * G * a.Dv;
+    out_l = a.ws_lse + (int64_t)wg * G;
+  }
+  ostride_head = a.Dv;
+  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
+    const int hd = idx / kD, dv = idx % kD;
+    float M = s_m[0][hd];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hd]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(s_m[w][hd] - M);
+        num += f * s_acc[w][hd][dv];
+        den += f * s_l[w][hd];
+      }
+    }
+    out_o[hd * ostride_head + dv] = den > 0.f ? num / den : 0.f;
+    if (dv == 0) out_l[hd] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  }
+  if (direct) return;
+
+  // ---- the last workgroup of this slice folds the splits
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  unsigned* ctr = a.counters + ((int64_t)b * a.Hkv + g) * a.P + r;
+  if (threadIdx.x == 0) s_last = (atomicAdd(ctr, 1u) == (unsigned)(nsplit - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int rec0 = wg - split;
+  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
+    const int hd = idx / kD, dv = idx % kD;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(a.ws_lse + (int64_t)(rec0 + s) * G + hd));
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float l = __builtin_nontemporal_load(a.ws_lse + (int64_t)(rec0 + s) * G + hd);
+        const float f = __builtin_amdgcn_exp2f((l - M) * 1.44269504088896341f);
+        num += f * __builtin_nontemporal_load(a.ws_o + ((int64_t)(rec0 + s) * G + hd) * a.Dv + dv);
+        den += f;
+      }
+    }
+    a.o_part[(((int64_t)r * a.Btot + b) * a.Hq + g * G + hd) * a.Dv + dv] = den > 0.f ? num / den : 0.f;
+    if (dv == 0) a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + hd] = den > 0.f ? M + __log2f(den) * kLn2 : -INFINITY;
+  }
+  if (threadIdx.x == 0) *ctr = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st) {
+  const int nwg = a.wg_begin[a.nb];
+  if (nwg == 0) return hipSuccess;
+  switch (dtype) {
+    case HX_KV_BF16:
+      hipLaunchKernelGGL(gqa_partial_kernel<0>, dim3(nwg), dim3(kThreads), 0, st, a);
+      break;
+    case HX_KV_FP8_E4M3:
+      hipLaunchKernelGGL(gqa_partial_kernel<1>, dim3(nwg), dim3(kThreads), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL(gqa_partial_kernel<2>, dim3(nwg), dim3(kThreads), 0, st, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hx

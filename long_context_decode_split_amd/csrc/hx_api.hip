@@ -1,0 +1,417 @@
+// C-ABI entry points of helixdecode: argument checks on the host, geometry,
+// the split policy, and the launches.  Nothing here allocates device memory.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+
+#include "hx_common.h"
+
+namespace hx {
+
+static thread_local char g_err[512] = "";
+
+hx_status fail(hx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hx_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HX_OK;
+  return fail(HX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hx_status geometry(const hx_kv_desc& d, Geometry* g) {
+  if (d.P < 1 || d.P > 64) return fail(HX_EINVAL, "P=%d must be in 1..64", d.P);
+  if (d.B < 1) return fail(HX_EINVAL, "B=%d must be >= 1", d.B);
+  if (d.Hkv < 1) return fail(HX_EINVAL, "Hkv=%d must be >= 1", d.Hkv);
+  if (d.cap < kChunk || d.cap % kChunk) return fail(HX_EINVAL, "cap=%lld must be a positive multiple of 16", (long long)d.cap);
+  if (d.reserved != 0) return fail(HX_EINVAL, "reserved must be 0");
+  if (d.dtype < HX_KV_BF16 || d.dtype > HX_KV_MXFP4) return fail(HX_EINVAL, "unknown dtype %d", d.dtype);
+  if (d.v_alias_k != 0 && d.v_alias_k != 1) return fail(HX_EINVAL, "v_alias_k must be 0 or 1");
+  if (d.Dk < 1 || d.Dv < 1) return fail(HX_EINVAL, "Dk and Dv must be positive");
+  Geometry t{};
+  if (d.Dk == 128 && d.Dv == 128 && !d.v_alias_k) {
+    t.kind = 0;
+    if (d.dtype == HX_KV_BF16) {
+      t.lay_k = kLayGqaBf16K; t.lay_v = kLayGqaBf16V; t.ebits = 16;
+      t.k_tile = t.v_tile = 4096; t.ks_tile = t.vs_tile = 0;
+    } else if (d.dtype == HX_KV_FP8_E4M3) {
+      t.lay_k = kLayGqaFp8K; t.lay_v = kLayGqaFp8V; t.ebits = 8;
+      t.k_tile = t.v_tile = 2048; t.ks_tile = t.vs_tile = 4;
+    } else {
+      t.lay_k = kLayGqaFp4K; t.lay_v = kLayGqaFp4V; t.ebits = 4;
+      t.k_tile = t.v_tile = 1024; t.ks_tile = t.vs_tile = 16 * (128 / 32);
+    }
+  } else if (d.Dk == 576 && d.Dv == 512 && d.v_alias_k && d.dtype == HX_KV_BF16) {
+    t.kind = 1;
+    t.lay_k = kLayRowBf16; t.lay_v = -1; t.ebits = 16;
+    t.k_tile = (int64_t)kChunk * 576 * 2; t.v_tile = 0; t.ks_tile = t.vs_tile = 0;
+  } else {
+    return fail(HX_EUNSUPPORTED, "unsupported cache: Dk=%d Dv=%d v_alias_k=%d dtype=%d", d.Dk, d.Dv, d.v_alias_k,
+                d.dtype);
+  }
+  const double tiles = (double)d.P * d.B * d.Hkv * (double)(d.cap / kChunk);
+  if (tiles * (double)t.k_tile > 9.0e18) return fail(HX_EINVAL, "cache too large");
+  t.tiles = (int64_t)d.P * d.B * d.Hkv * (d.cap / kChunk);
+  *g = t;
+  return HX_OK;
+}
+
+// ---------------------------------------------------------------- split policy
+static int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  const int v = atoi(s);
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+static int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int target_wgs(int kind) {
+  // Workgroups per CU for one launch; HX_WGS_PER_CU overrides (tuning knob).
+  const int per_cu = env_int("HX_WGS_PER_CU", kind == 0 ? 4 : 2, 1, 8);
+  const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
+  return std::min(bound, device_cus() * per_cu);
+}
+
+int min_chunks_per_wg(int kind) { return kind == 0 ? 4 * kGqaWavesPerWg : 4; }
+
+static int64_t ws_records(const hx_kv_desc& d, int kind) {
+  const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
+  return (int64_t)bound + (int64_t)d.Hkv * d.P * std::min(d.B, kMaxBatchPerLaunch);
+}
+
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct WsLayout {
+  int64_t counters_off, o_off, lse_off, total;
+};
+
+static WsLayout ws_layout(const hx_kv_desc& d, int kind, int G) {
+  WsLayout w;
+  const int64_t recs = ws_records(d, kind);
+  w.counters_off = 0;
+  w.o_off = align256((int64_t)d.B * d.Hkv * d.P * 4);
+  w.lse_off = w.o_off + align256(recs * G * d.Dv * 4);
+  w.total = w.lse_off + align256(recs * G * 4);
+  return w;
+}
+
+}  // namespace hx
+
+using namespace hx;
+
+extern "C" {
+
+const char* hx_last_error(void) { return g_err; }
+
+const char* hx_version(void) { return "helixdecode 0.1 (gfx950)"; }
+
+hx_status hx_kv_layout(const hx_kv_desc* desc, hx_kv_layout_info* out) {
+  g_err[0] = 0;
+  if (!desc || !out) return fail(HX_EINVAL, "null argument");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  out->k_tile_bytes = (size_t)g.k_tile;
+  out->v_tile_bytes = (size_t)g.v_tile;
+  out->k_bytes = (size_t)(g.tiles * g.k_tile);
+  out->v_bytes = (size_t)(g.tiles * g.v_tile);
+  out->k_scale_bytes = (size_t)(g.tiles * g.ks_tile);
+  out->v_scale_bytes = (size_t)(g.tiles * g.vs_tile);
+  out->n_max = (int64_t)desc->P * desc->cap;
+  return HX_OK;
+}
+
+hx_status hx_slot(int64_t t, int32_t P, int32_t* r, int64_t* j) {
+  g_err[0] = 0;
+  if (!r || !j) return fail(HX_EINVAL, "null argument");
+  if (t < 0 || P < 1) return fail(HX_EINVAL, "t=%lld must be >= 0 and P=%d >= 1", (long long)t, P);
+  const int64_t c = t / kChunk;
+  *r = (int32_t)(c % P);
+  *j = (c / P) * kChunk + t % kChunk;
+  return HX_OK;
+}
+
+hx_status hx_slice_len(int64_t n, int32_t P, int32_t r, int64_t* len) {
+  g_err[0] = 0;
+  if (!len) return fail(HX_EINVAL, "null argument");
+  if (n < 0 || P < 1 || r < 0 || r >= P) return fail(HX_EINVAL, "need n >= 0, P >= 1, 0 <= r < P");
+  *len = slice_len(n, P, r);
+  return HX_OK;
+}
+
+hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, int32_t d, int64_t* off2) {
+  g_err[0] = 0;
+  if (!desc || !off2) return fail(HX_EINVAL, "null argument");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  if (which != 0 && which != 1) return fail(HX_EINVAL, "which must be 0 (K) or 1 (V)");
+  const int width = which == 0 ? desc->Dk : desc->Dv;
+  if (m < 0 || m >= kChunk || d < 0 || d >= width) return fail(HX_EINVAL, "element out of the tile");
+  const int lay = (which == 1 && !desc->v_alias_k) ? g.lay_v : g.lay_k;
+  *off2 = tile_off2(lay, desc->Dk, m, d);
+  return HX_OK;
+}
+
+hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                       const void* k_scale_new, const void* v_scale_new, const int64_t* pos, const int32_t* count,
+                       int32_t n_new, void* stream) {
+  g_err[0] = 0;
+  if (!desc || !cache || !pos) return fail(HX_EINVAL, "null argument");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  const hx_kv_desc& d = *desc;
+  if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
+  const bool alias = d.v_alias_k;
+  const bool scaled = d.dtype != HX_KV_BF16;
+  if (!cache->k || !k_new) return fail(HX_EINVAL, "null K plane or k_new");
+  if (!alias && (!cache->v || !v_new)) return fail(HX_EINVAL, "null V plane or v_new");
+  if (alias && (v_new || cache->v)) return fail(HX_EINVAL, "v_new and cache->v must be NULL when v_alias_k = 1");
+  if (scaled && (!cache->k_scale || !k_scale_new || (!alias && (!cache->v_scale || !v_scale_new))))
+    return fail(HX_EINVAL, "null scale plane or scale input");
+  if (!scaled && (k_scale_new || v_scale_new)) return fail(HX_EINVAL, "bf16 caches take no scales");
+  const void* ptrs[8] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_new, v_new, k_scale_new, v_scale_new};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  const int64_t nmax = (int64_t)d.P * d.cap;
+  for (int b = 0; b < d.B; ++b) {
+    const int32_t cnt = count ? count[b] : n_new;
+    if (cnt < 0 || cnt > n_new) return fail(HX_EINVAL, "request %d: count=%d must be in [0, n_new=%d]", b, cnt, n_new);
+    if (pos[b] < 0 || pos[b] + cnt > nmax)
+      return fail(HX_EINVAL, "request %d: pos=%lld, count=%d exceeds P*cap=%lld", b, (long long)pos[b], cnt,
+                  (long long)nmax);
+  }
+
+  AppendArgs a{};
+  int np = 0;
+  auto add = [&](const void* src, void* dst, int lay, int width, int ebits, int64_t row_bytes, int64_t tile_bytes) {
+    a.src[np] = (const uint8_t*)src;
+    a.dst[np] = (uint8_t*)dst;
+    a.lay[np] = lay;
+    a.width[np] = width;
+    a.ebits[np] = ebits;
+    a.src_row_bytes[np] = row_bytes;
+    a.tile_bytes[np] = tile_bytes;
+    ++np;
+  };
+  add(k_new, cache->k, g.lay_k, d.Dk, g.ebits, (int64_t)d.Dk * g.ebits / 8, g.k_tile);
+  if (!alias) add(v_new, cache->v, g.lay_v, d.Dv, g.ebits, (int64_t)d.Dv * g.ebits / 8, g.v_tile);
+  if (d.dtype == HX_KV_FP8_E4M3) {
+    add(k_scale_new, cache->k_scale, kLayRowU8, 1, 32, 4, 4);
+    if (!alias) add(v_scale_new, cache->v_scale, kLayRowU8, 1, 32, 4, 4);
+  } else if (d.dtype == HX_KV_MXFP4) {
+    add(k_scale_new, cache->k_scale, kLayRowU8, d.Dk / 32, 8, d.Dk / 32, g.ks_tile);
+    if (!alias) add(v_scale_new, cache->v_scale, kLayRowU8, d.Dv / 32, 8, d.Dv / 32, g.vs_tile);
+  }
+  a.nplanes = np;
+  a.P = d.P;
+  a.B = d.B;
+  a.Hkv = d.Hkv;
+  a.cap_chunks = d.cap / kChunk;
+  a.n_new = n_new;
+  const uint8_t* src0[4];
+  for (int p = 0; p < np; ++p) src0[p] = a.src[p];
+  for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
+    int maxc = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int64_t p0 = pos[b0 + i];
+      const int32_t cnt = count ? count[b0 + i] : n_new;
+      a.pos[i] = p0;
+      a.count[i] = cnt;
+      if (cnt > 0) maxc = std::max(maxc, (int)((p0 + cnt - 1) / kChunk - p0 / kChunk + 1));
+    }
+    a.max_chunks = maxc;
+    a.b0 = b0;
+    for (int p = 0; p < np; ++p) a.src[p] = src0[p] + (int64_t)b0 * d.Hkv * n_new * a.src_row_bytes[p];
+    s = check_hip(launch_append(a, nb, (hipStream_t)stream), "kv_append launch");
+    if (s) return s;
+  }
+  return HX_OK;
+}
+
+hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
+                        int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
+  g_err[0] = 0;
+  if (!desc || !cache || !k_out) return fail(HX_EINVAL, "null argument");
+  Geometry geo;
+  hx_status s = geometry(*desc, &geo);
+  if (s) return s;
+  const hx_kv_desc& d = *desc;
+  if (r < 0 || r >= d.P || b < 0 || b >= d.B || g < 0 || g >= d.Hkv) return fail(HX_EINVAL, "(r, b, g) out of range");
+  if (j0 < 0 || n < 0 || j0 + n > d.cap) return fail(HX_EINVAL, "rows [j0, j0+n) must lie in [0, cap)");
+  if (!cache->k || (!d.v_alias_k && !cache->v)) return fail(HX_EINVAL, "null cache plane");
+  if (d.dtype != HX_KV_BF16 && (!cache->k_scale || (!d.v_alias_k && !cache->v_scale)))
+    return fail(HX_EINVAL, "null scale plane");
+  const void* ptrs[6] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_out, v_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  DequantArgs a{};
+  a.k = (const uint8_t*)cache->k;
+  a.v = (const uint8_t*)cache->v;
+  a.ks = (const uint8_t*)cache->k_scale;
+  a.vs = (const uint8_t*)cache->v_scale;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.dtype = d.dtype;
+  a.lay_k = geo.lay_k;
+  a.lay_v = geo.lay_v;
+  a.Dk = d.Dk;
+  a.Dv = d.Dv;
+  a.v_alias = d.v_alias_k;
+  a.k_tile = geo.k_tile;
+  a.v_tile = geo.v_tile;
+  a.ks_tile = geo.ks_tile;
+  a.vs_tile = geo.vs_tile;
+  a.plane_tile0 = ((int64_t)(r * d.B + b) * d.Hkv + g) * (d.cap / kChunk);
+  a.j0 = j0;
+  a.n = n;
+  return check_hip(launch_dequant(a, (hipStream_t)stream), "kv_dequant launch");
+}
+
+static hx_status check_heads(const hx_kv_desc& d, const Geometry& geo, int32_t Hq) {
+  if (Hq < 1 || Hq % d.Hkv) return fail(HX_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", Hq, d.Hkv);
+  const int G = Hq / d.Hkv;
+  if (geo.kind == 0 && G > 16) return fail(HX_EUNSUPPORTED, "GQA kernel takes at most 16 query heads per KV head (G=%d)", G);
+  if (geo.kind == 1 && G != 128) return fail(HX_EUNSUPPORTED, "MLA kernel takes 128 query heads per latent head (G=%d)", G);
+  return HX_OK;
+}
+
+hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes) {
+  g_err[0] = 0;
+  if (!desc || !bytes) return fail(HX_EINVAL, "null argument");
+  Geometry geo;
+  hx_status s = geometry(*desc, &geo);
+  if (s) return s;
+  s = check_heads(*desc, geo, Hq);
+  if (s) return s;
+  *bytes = (size_t)ws_layout(*desc, geo.kind, Hq / desc->Hkv).total;
+  return HX_OK;
+}
+
+hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!ws || !aligned16(ws)) return fail(HX_EINVAL, "workspace must be a non-null 16-byte aligned pointer");
+  return check_hip(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream), "workspace memset");
+}
+
+hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                                 const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!desc || !cache || !q || !ctx_len || !o_part || !lse_part || !ws) return fail(HX_EINVAL, "null argument");
+  Geometry geo;
+  hx_status s = geometry(*desc, &geo);
+  if (s) return s;
+  const hx_kv_desc& d = *desc;
+  s = check_heads(d, geo, Hq);
+  if (s) return s;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(HX_EINVAL, "scale must be finite and > 0");
+  if (!cache->k || (!d.v_alias_k && !cache->v)) return fail(HX_EINVAL, "null cache plane");
+  if (d.dtype != HX_KV_BF16 && (!cache->k_scale || (!d.v_alias_k && !cache->v_scale)))
+    return fail(HX_EINVAL, "null scale plane");
+  const void* ptrs[8] = {cache->k, cache->v, cache->k_scale, cache->v_scale, q, o_part, lse_part, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  const int G = Hq / d.Hkv;
+  const WsLayout wl = ws_layout(d, geo.kind, G);
+  if ((int64_t)ws_bytes < wl.total)
+    return fail(HX_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)wl.total);
+  const int64_t nmax = (int64_t)d.P * d.cap;
+  for (int b = 0; b < d.B; ++b)
+    if (ctx_len[b] < 1 || ctx_len[b] > nmax)
+      return fail(HX_EINVAL, "ctx_len[%d]=%lld must be in [1, P*cap=%lld]", b, (long long)ctx_len[b], (long long)nmax);
+
+  PartialArgs a{};
+  a.k = (const uint8_t*)cache->k;
+  a.v = (const uint8_t*)(d.v_alias_k ? cache->k : cache->v);
+  a.ks = (const uint8_t*)cache->k_scale;
+  a.vs = (const uint8_t*)(d.v_alias_k ? cache->k_scale : cache->v_scale);
+  a.q = (const uint16_t*)q;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.counters = (unsigned*)((uint8_t*)ws + wl.counters_off);
+  a.ws_o = (float*)((uint8_t*)ws + wl.o_off);
+  a.ws_lse = (float*)((uint8_t*)ws + wl.lse_off);
+  a.P = d.P;
+  a.Btot = d.B;
+  a.Hkv = d.Hkv;
+  a.Hq = Hq;
+  a.G = G;
+  a.Dk = d.Dk;
+  a.Dv = d.Dv;
+  a.cap_chunks = d.cap / kChunk;
+  a.k_tile = geo.k_tile;
+  a.v_tile = d.v_alias_k ? geo.k_tile : geo.v_tile;
+  a.ks_tile = geo.ks_tile;
+  a.vs_tile = d.v_alias_k ? geo.ks_tile : geo.vs_tile;
+  a.c2 = scale * 1.44269504088896341f;
+  const int64_t records = ws_records(d, geo.kind);
+  const int target = target_wgs(geo.kind);
+  const int minc = min_chunks_per_wg(geo.kind);
+  for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
+    int64_t W = 0;
+    int64_t nch[kMaxBatchPerLaunch];
+    for (int i = 0; i < nb; ++i) {
+      a.n[i] = ctx_len[b0 + i];
+      nch[i] = (slice_len(a.n[i], d.P, 0) + kChunk - 1) / kChunk;   // slice 0 is never shorter
+      W += nch[i] * d.Hkv * d.P;
+    }
+    int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
+    a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
+    int wgs = 0;
+    for (int i = 0; i < nb; ++i) {
+      a.nsplit[i] = (int)((nch[i] + a.cpw - 1) / a.cpw);
+      a.wg_begin[i] = wgs;
+      wgs += a.nsplit[i] * d.Hkv * d.P;
+    }
+    a.wg_begin[nb] = wgs;
+    if (wgs > records) return fail(HX_EINVAL, "internal: %d workgroups exceed the %lld workspace records", wgs, (long long)records);
+    a.b0 = b0;
+    a.nb = nb;
+    hipError_t e = geo.kind == 0 ? launch_gqa_partial(a, d.dtype, (hipStream_t)stream)
+                                 : launch_mla_partial(a, (hipStream_t)stream);
+    s = check_hip(e, "decode_attn_partial launch");
+    if (s) return s;
+  }
+  return HX_OK;
+}
+
+hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,
+                         float* o, float* lse, void* stream) {
+  g_err[0] = 0;
+  if (!o_part || !lse_part || !o || !lse) return fail(HX_EINVAL, "null argument");
+  if (P < 1 || P > 1024 || B < 1 || Hq < 1 || Dv < 1) return fail(HX_EINVAL, "need 1 <= P <= 1024 and B, Hq, Dv >= 1");
+  const void* ptrs[4] = {o_part, lse_part, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  return check_hip(launch_lse_combine(P, B, Hq, Dv, o_part, lse_part, o, lse, (hipStream_t)stream), "lse_combine launch");
+}
+
+}  // extern "C"

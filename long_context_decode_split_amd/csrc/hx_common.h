@@ -1,0 +1,228 @@
+// Internal declarations shared by the helixdecode HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "helixdecode.h"
+
+#define HXHD __host__ __device__ __forceinline__
+
+namespace hx {
+
+constexpr int kChunk = HX_CHUNK;   // rows per chunk tile, the placement unit
+constexpr int kMaxBatchPerLaunch = 64;
+
+// ---------------------------------------------------------------- placement
+// Token t of a request: group t/16 goes to slice (t/16) mod P as that
+// slice's ((t/16)/P)-th group (Helix summary, paragraph on Helix's two
+// layouts; NVIDIA blog, section on distributed KV placement).
+HXHD int64_t slice_len(int64_t n, int P, int r) {
+  const int64_t round = (int64_t)kChunk * P;
+  const int64_t full = n / round;
+  int64_t left = n - full * round - (int64_t)kChunk * r;
+  left = left < 0 ? 0 : (left > kChunk ? kChunk : left);
+  return full * kChunk + left;
+}
+
+// ---------------------------------------------------------------- tile layouts
+// A cache plane is [P][B][Hkv][cap/16] tiles; a tile holds 16 rows.  The
+// byte order inside a tile is chosen so that one 16-byte load per lane of a
+// 64-lane wave fetches exactly the matrix-core operand fragment a lane
+// needs, and every wave-wide load instruction reads 1 KiB contiguous:
+//
+//  * K tiles feed v_mfma_f32_16x16x32_bf16 as the A operand (rows = 16
+//    tokens, k = 32 columns of d per step s): lane l = 16*h + m holds token m,
+//    columns 32*s + 8*h .. +7.
+//  * V tiles feed v_mfma_f32_16x16x16_bf16 as the A operand of O^T = V^T P^T
+//    (rows = 16 columns of dv in block nb, k = 16 tokens): lane l = 16*hq + c
+//    holds column 16*nb + c of tokens 4*hq .. 4*hq+3.
+//
+// Layout ids:
+enum Layout : int {
+  kLayGqaBf16K = 0, kLayGqaBf16V = 1,
+  kLayGqaFp8K = 2, kLayGqaFp8V = 3,
+  kLayGqaFp4K = 4, kLayGqaFp4V = 5,
+  kLayRowBf16 = 6,   // plain row-major bf16 rows (MLA latent rows)
+  kLayRowU8 = 7,     // plain row-major bytes (MXFP4 e8m0 scale rows)
+};
+
+// Element (row m, column d) -> 2 * byte offset + nibble (nibble is 1 for the
+// high half of an FP4 byte).  `width` is the row width for row layouts.
+HXHD int64_t tile_off2(int lay, int width, int m, int d) {
+  switch (lay) {
+    case kLayGqaBf16K: {
+      const int s = d >> 5, h = (d >> 3) & 3, e = d & 7;
+      return 2 * (int64_t)(s * 1024 + (h * 16 + m) * 16 + e * 2);
+    }
+    case kLayGqaBf16V: {
+      const int nb = d >> 4, c = d & 15, hq = m >> 2, j = m & 3;
+      return 2 * (int64_t)((nb >> 1) * 1024 + (hq * 16 + c) * 16 + (nb & 1) * 8 + j * 2);
+    }
+    case kLayGqaFp8K: {
+      const int s = d >> 5, h = (d >> 3) & 3, e = d & 7;
+      return 2 * (int64_t)((s >> 1) * 1024 + (h * 16 + m) * 16 + (s & 1) * 8 + e);
+    }
+    case kLayGqaFp8V: {
+      const int nb = d >> 4, c = d & 15, hq = m >> 2, j = m & 3;
+      return 2 * (int64_t)((nb >> 2) * 1024 + (hq * 16 + c) * 16 + (nb & 3) * 4 + j);
+    }
+    case kLayGqaFp4K: {
+      const int s = d >> 5, h = (d >> 3) & 3, e = d & 7;
+      const int ni = s * 8 + e;
+      return 2 * (int64_t)((h * 16 + m) * 16 + (ni >> 1)) + (ni & 1);
+    }
+    case kLayGqaFp4V: {
+      const int nb = d >> 4, c = d & 15, hq = m >> 2, j = m & 3;
+      const int ni = nb * 4 + j;
+      return 2 * (int64_t)((hq * 16 + c) * 16 + (ni >> 1)) + (ni & 1);
+    }
+    case kLayRowBf16:
+      return 2 * ((int64_t)m * width + d) * 2;
+    case kLayRowU8:
+    default:
+      return 2 * ((int64_t)m * width + d);
+  }
+}
+
+// Inverse: (2 * byte offset + nibble) of an element -> (m, d).  Used by the
+// append kernel, which owns destination bytes.  `ebits` is the element size.
+HXHD void tile_inv(int lay, int width, int64_t off2, int* m, int* d) {
+  const int b = (int)(off2 >> 1);
+  const int nib = (int)(off2 & 1);
+  switch (lay) {
+    case kLayGqaBf16K: {
+      const int s = b >> 10, lane = (b >> 4) & 63, e = (b >> 1) & 7;
+      *m = lane & 15;
+      *d = s * 32 + (lane >> 4) * 8 + e;
+      return;
+    }
+    case kLayGqaBf16V: {
+      const int p = b >> 10, lane = (b >> 4) & 63, w = (b >> 1) & 7;
+      *m = (lane >> 4) * 4 + (w & 3);
+      *d = (2 * p + (w >> 2)) * 16 + (lane & 15);
+      return;
+    }
+    case kLayGqaFp8K: {
+      const int i = b >> 10, lane = (b >> 4) & 63, w = b & 15;
+      const int s = 2 * i + (w >> 3);
+      *m = lane & 15;
+      *d = s * 32 + (lane >> 4) * 8 + (w & 7);
+      return;
+    }
+    case kLayGqaFp8V: {
+      const int i = b >> 10, lane = (b >> 4) & 63, w = b & 15;
+      *m = (lane >> 4) * 4 + (w & 3);
+      *d = (4 * i + (w >> 2)) * 16 + (lane & 15);
+      return;
+    }
+    case kLayGqaFp4K: {
+      const int lane = b >> 4, ni = (b & 15) * 2 + nib;
+      *m = lane & 15;
+      *d = (ni >> 3) * 32 + (lane >> 4) * 8 + (ni & 7);
+      return;
+    }
+    case kLayGqaFp4V: {
+      const int lane = b >> 4, ni = (b & 15) * 2 + nib;
+      *m = (lane >> 4) * 4 + (ni & 3);
+      *d = (ni >> 2) * 16 + (lane & 15);
+      return;
+    }
+    case kLayRowBf16:
+      *m = (b >> 1) / width;
+      *d = (b >> 1) % width;
+      return;
+    case kLayRowU8:
+    default:
+      *m = b / width;
+      *d = b % width;
+      return;
+  }
+}
+
+// ---------------------------------------------------------------- cache geometry
+struct Geometry {
+  int kind;            // 0 GQA (Dk = Dv = 128), 1 MLA (576 / 512, aliased, bf16)
+  int lay_k, lay_v;    // tile layouts of the K and V code planes
+  int ebits;           // bits per code element: 16, 8 or 4
+  int64_t k_tile, v_tile;          // bytes per chunk tile
+  int64_t ks_tile, vs_tile;        // bytes of scale per chunk tile (0 = none)
+  int64_t tiles;                   // P * B * Hkv * cap / 16
+};
+
+// Fills `g` from a validated descriptor; returns HX_EUNSUPPORTED for a
+// combination with no kernel.
+hx_status geometry(const hx_kv_desc& d, Geometry* g);
+
+// Error reporting (thread-local message).
+hx_status fail(hx_status s, const char* fmt, ...);
+hx_status check_hip(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------- launchers
+struct AppendArgs {
+  const uint8_t* src[4];   // k codes, v codes, k scales, v scales (token-major)
+  uint8_t* dst[4];         // planes
+  int lay[4];              // tile layout per plane
+  int width[4];            // row width (row layouts)
+  int ebits[4];            // element bits per plane (16, 8, 4; 32 = fp8 group scale)
+  int64_t src_row_bytes[4];
+  int64_t tile_bytes[4];
+  int nplanes;
+  int P, B, Hkv;
+  int64_t cap_chunks;
+  int n_new;
+  int max_chunks;          // largest number of chunks one request touches
+  int64_t pos[kMaxBatchPerLaunch];
+  int32_t count[kMaxBatchPerLaunch];
+  int b0;                  // first request of this launch
+};
+hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st);
+
+struct DequantArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  float* k_out;
+  float* v_out;
+  int dtype, lay_k, lay_v, Dk, Dv, v_alias;
+  int64_t k_tile, v_tile, ks_tile, vs_tile;
+  int64_t plane_tile0;     // tile index of (r, b, g, chunk 0)
+  int64_t j0, n;
+};
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
+
+struct PartialArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  const uint16_t* q;       // bf16 bits [Btot][Hq][Dk]
+  float* o_part;           // [P][Btot][Hq][Dv]
+  float* lse_part;         // [P][Btot][Hq]
+  float* ws_o;             // [records][G][Dv]
+  float* ws_lse;           // [records][G]
+  unsigned* counters;      // [Btot][Hkv][P]
+  int P, Btot, b0, nb, Hkv, Hq, G, Dk, Dv;
+  int64_t cap_chunks;
+  int64_t k_tile, v_tile, ks_tile, vs_tile;
+  float c2;                // softmax scale * log2(e)
+  int cpw;                 // chunks per workgroup (split size)
+  int64_t n[kMaxBatchPerLaunch];
+  int nsplit[kMaxBatchPerLaunch];
+  int wg_begin[kMaxBatchPerLaunch + 1];
+};
+hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
+hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
+
+hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part, const float* lse_part, float* o,
+                              float* lse, hipStream_t st);
+
+// Split policy shared by hx_workspace_size and hx_decode_attn_partial.
+constexpr int kGqaWavesPerWg = 4;
+constexpr int kGqaTargetWgs = 2048;   // upper bound on the split target
+constexpr int kMlaTargetWgs = 1024;
+int target_wgs(int kind);            // device-dependent, <= the bounds above
+int min_chunks_per_wg(int kind);
+
+}  // namespace hx

@@ -1,0 +1,227 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-only entry points and argument checks behave.
+
+No test here launches device work on purpose; the one call that would launch
+runs only when no GPU is present and must come back as HX_EHIP."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_split_amd import _lib, api
+from oracle import placement
+from tests.helpers import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "helixdecode.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    ensure_built()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(_lib.SIGNATURES), (declared_symbols(), sorted(_lib.SIGNATURES))
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\b(hx_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [s for s in declared_symbols() if s not in exported]
+    assert not missing, missing
+    lib = _lib.lib()
+    for s in declared_symbols():
+        assert getattr(lib, s) is not None
+
+
+def test_version():
+    assert "gfx950" in api.version()
+
+
+def test_slot_matches_oracle():
+    for P in (1, 2, 3, 4, 8, 13, 64):
+        for t in list(range(0, 600)) + [2**20 - 1, 2**20, 2**31 + 7]:
+            assert api.slot(t, P) == placement.slot(t, P), (t, P)
+
+
+def test_slice_len_matches_oracle():
+    for P in (1, 2, 4, 8, 13):
+        for n in list(range(0, 400)) + [4096, 4137, 2**20, 2097152, 1234567]:
+            for r in range(P):
+                assert api.slice_len(n, P, r) == placement.slice_len(n, P, r)
+
+
+def test_slot_errors():
+    with pytest.raises(api.HXError) as e:
+        api.slot(-1, 4)
+    assert e.value.status == _lib.HX_EINVAL
+    with pytest.raises(api.HXError):
+        api.slot(3, 0)
+    with pytest.raises(api.HXError):
+        api.slice_len(5, 4, 4)
+
+
+DESCS = [
+    api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64),
+    api.KVDesc(P=8, B=3, Hkv=2, Dk=128, Dv=128, v_alias_k=False, dtype="fp8_e4m3", cap=32),
+    api.KVDesc(P=8, B=1, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="mxfp4", cap=48),
+    api.KVDesc(P=2, B=1, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="bf16", cap=16),
+]
+
+
+@pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.dtype}-{d.Dk}")
+def test_layout_sizes(desc):
+    lay = api.kv_layout(desc)
+    tiles = desc.P * desc.B * desc.Hkv * desc.cap // 16
+    bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
+    assert lay["k_tile_bytes"] == 16 * desc.Dk * bits // 8
+    assert lay["k_bytes"] == tiles * lay["k_tile_bytes"]
+    if desc.v_alias_k:
+        assert lay["v_bytes"] == 0
+    else:
+        assert lay["v_bytes"] == tiles * 16 * desc.Dv * bits // 8
+    scale = {"bf16": 0, "fp8_e4m3": 4, "mxfp4": 16 * desc.Dk // 32}[desc.dtype]
+    assert lay["k_scale_bytes"] == tiles * scale
+    assert lay["n_max"] == desc.P * desc.cap
+
+
+@pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.dtype}-{d.Dk}")
+def test_tile_layout_is_a_bijection(desc):
+    lay = api.kv_layout(desc)
+    for which, width, tile in ((0, desc.Dk, lay["k_tile_bytes"]), (1, desc.Dv, lay["v_tile_bytes"])):
+        if which == 1 and desc.v_alias_k:
+            continue
+        bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
+        offs = set()
+        for m in range(16):
+            for d in range(width):
+                o2 = api.kv_tile_offset(desc, which, m, d)
+                if bits == 16:
+                    assert o2 % 4 == 0
+                elif bits == 8:
+                    assert o2 % 2 == 0
+                offs.add(o2 // {16: 4, 8: 2, 4: 1}[bits])
+        assert offs == set(range(tile * 8 // bits)), "elements must fill the tile exactly once"
+
+
+def test_gqa_bf16_tile_gives_lane_fragments():
+    """Each 1 KiB of a K tile is one wave-wide 16-byte-per-lane load: lane
+    16h+m holds token m, columns 32s+8h..+7 of step s."""
+    desc = DESCS[0]
+    for s in range(4):
+        for lane in range(64):
+            m, h = lane % 16, lane // 16
+            for e in range(8):
+                assert api.kv_tile_offset(desc, 0, m, 32 * s + 8 * h + e) // 2 == s * 1024 + lane * 16 + 2 * e
+
+
+def test_tile_offset_errors():
+    with pytest.raises(api.HXError):
+        api.kv_tile_offset(DESCS[0], 0, 16, 0)
+    with pytest.raises(api.HXError):
+        api.kv_tile_offset(DESCS[0], 2, 0, 0)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(P=0), _lib.HX_EINVAL), (dict(P=65), _lib.HX_EINVAL), (dict(cap=40), _lib.HX_EINVAL),
+    (dict(cap=0), _lib.HX_EINVAL), (dict(B=0), _lib.HX_EINVAL), (dict(Dk=64, Dv=64), _lib.HX_EUNSUPPORTED),
+    (dict(Dk=576, Dv=512, v_alias_k=False), _lib.HX_EUNSUPPORTED),
+    (dict(Dk=576, Dv=512, v_alias_k=True, dtype="fp8_e4m3"), _lib.HX_EUNSUPPORTED),
+])
+def test_desc_errors(bad, status):
+    base = dict(P=4, B=1, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    base.update(bad)
+    with pytest.raises(api.HXError) as e:
+        api.kv_layout(api.KVDesc(**base))
+    assert e.value.status == status
+    assert _lib.lib().hx_last_error().decode()
+
+
+def test_workspace_size_and_heads():
+    d = DESCS[0]
+    assert api.workspace_size(d, 8) > 0
+    with pytest.raises(api.HXError) as e:
+        api.workspace_size(d, 17 * 2)   # G = 34 > 16
+    assert e.value.status == _lib.HX_EUNSUPPORTED
+    with pytest.raises(api.HXError) as e:
+        api.workspace_size(DESCS[1], 3)   # not a multiple of Hkv = 2
+    assert e.value.status == _lib.HX_EINVAL
+    with pytest.raises(api.HXError) as e:
+        api.workspace_size(DESCS[3], 64)   # MLA takes G = 128
+    assert e.value.status == _lib.HX_EUNSUPPORTED
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _partial(desc, ctx, q=0x10000, ws=0x20000, ws_bytes=1 << 30, scale=0.1, Hq=8, o=0x30000, lse=0x40000,
+             cache=None):
+    L = _lib.lib()
+    cache = cache or _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+    ctx_arr = (ctypes.c_int64 * len(ctx))(*ctx)
+    return L.hx_decode_attn_partial(ctypes.byref(desc.c()), ctypes.byref(cache), _fake(q), Hq, ctx_arr,
+                                    ctypes.c_float(scale), _fake(o), _fake(lse), _fake(ws), ws_bytes, None)
+
+
+def test_partial_argument_checks_return_before_launch():
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    assert _partial(d, [0, 5]) == _lib.HX_EINVAL            # empty context
+    assert _partial(d, [5, 4 * 64 + 1]) == _lib.HX_EINVAL   # beyond P * cap
+    assert _partial(d, [5, 5], q=0x10008) == _lib.HX_EINVAL  # misaligned
+    assert _partial(d, [5, 5], ws_bytes=16) == _lib.HX_EINVAL  # workspace too small
+    assert _partial(d, [5, 5], scale=0.0) == _lib.HX_EINVAL
+    assert _partial(d, [5, 5], scale=float("nan")) == _lib.HX_EINVAL
+    assert _partial(d, [5, 5], Hq=0) == _lib.HX_EINVAL
+    assert _partial(d, [5, 5], cache=_lib.hx_kv_cache(0x50000, None, None, None)) == _lib.HX_EINVAL
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_partial_without_device_is_hx_ehip():
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    assert _partial(d, [5, 17]) == _lib.HX_EHIP
+
+
+def test_append_argument_checks():
+    L = _lib.lib()
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+
+    def call(pos, count=None, n_new=4, k=0x10000, v=0x20000, ks=None):
+        pa = (ctypes.c_int64 * 2)(*pos)
+        ca = None if count is None else (ctypes.c_int32 * 2)(*count)
+        return L.hx_kv_append(ctypes.byref(d.c()), ctypes.byref(cache), _fake(k), _fake(v), ks, None, pa, ca, n_new,
+                              None)
+
+    assert call([0, 254]) == _lib.HX_EINVAL            # 254 + 4 > P * cap = 256
+    assert call([-1, 0]) == _lib.HX_EINVAL
+    assert call([0, 0], n_new=0) == _lib.HX_EINVAL
+    assert call([0, 0], count=[5, 1]) == _lib.HX_EINVAL   # count > n_new
+    assert call([0, 0], count=[-1, 1]) == _lib.HX_EINVAL
+    assert call([0, 0], k=0x10002) == _lib.HX_EINVAL      # misaligned
+    assert call([0, 0], v=0) == _lib.HX_EINVAL
+    assert call([0, 0], ks=_fake(0x70000)) == _lib.HX_EINVAL   # bf16 takes no scales
+
+
+def test_dequant_and_combine_argument_checks():
+    L = _lib.lib()
+    d = DESCS[0]
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+    assert L.hx_kv_dequant(ctypes.byref(d.c()), ctypes.byref(cache), 4, 0, 0, 0, 1, _fake(0x1000), None,
+                           None) == _lib.HX_EINVAL
+    assert L.hx_kv_dequant(ctypes.byref(d.c()), ctypes.byref(cache), 0, 0, 0, 60, 8, _fake(0x1000), None,
+                           None) == _lib.HX_EINVAL
+    assert L.hx_lse_combine(0, 1, 1, 1, _fake(16), _fake(32), _fake(48), _fake(64), None) == _lib.HX_EINVAL
+    assert L.hx_lse_combine(2, 1, 1, 1, _fake(16), _fake(33), _fake(48), _fake(64), None) == _lib.HX_EINVAL
+    assert L.hx_lse_combine(2, 1, 1, 1, None, _fake(32), _fake(48), _fake(64), None) == _lib.HX_EINVAL

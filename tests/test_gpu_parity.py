@@ -1,0 +1,280 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, at sizes the
+oracle finishes in seconds that still span several chunk tiles, several
+splits per slice and ragged tails.
+
+Bars: placement and dequantisation bit-exact; O within 2e-3 (bf16 KV) or
+2e-2 (fp8 / MXFP4 KV, oracle on the dequantised values) absolute and 1e-2 /
+5e-2 relative to max |O|; LSE within 1e-4 relative (helpers.TOL)."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_split_amd import api, configs, synth
+from oracle import attention as oatt
+from oracle import codecs as ocod
+from oracle import placement as opl
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    H.ensure_built()
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits_f32(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def _same_f32(a, b):
+    """Bit-exact equality of fp32 arrays, any NaN matching any NaN."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    return np.array_equal(na, nb) and np.array_equal(_bits_f32(a)[~na], _bits_f32(b)[~nb])
+
+
+# ---------------------------------------------------------------- cache writes and reads
+
+def _random_storage(w, ctx, seed):
+    """Arbitrary storage-format bytes (every bit pattern, NaN codes included)."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    nmax = max(ctx)
+    kb = {"bf16": 2 * w.Dk, "fp8_e4m3": w.Dk, "mxfp4": w.Dk // 2}[w.dtype]
+    vb = {"bf16": 2 * w.Dv, "fp8_e4m3": w.Dv, "mxfp4": w.Dv // 2}[w.dtype]
+    rnd = lambda *s: torch.randint(0, 256, s, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    k = rnd(w.B, w.Hkv, nmax, kb)
+    v = None if w.v_alias_k else rnd(w.B, w.Hkv, nmax, vb)
+    if w.dtype == "bf16":
+        k = k.view(torch.bfloat16)
+        v = None if v is None else v.view(torch.bfloat16)
+    ks = vs = None
+    if w.dtype == "fp8_e4m3":
+        # one positive scale per 16-token group, repeated per token
+        grp = torch.rand(w.B, w.Hkv, -(-nmax // 16), generator=g, device=DEV) * 4 + 0.01
+        ks = grp.repeat_interleave(16, dim=-1)[..., :nmax].contiguous()
+        vs = (grp * 0.5).repeat_interleave(16, dim=-1)[..., :nmax].contiguous()
+    elif w.dtype == "mxfp4":
+        ks = torch.randint(100, 160, (w.B, w.Hkv, nmax, w.Dk // 32), generator=g, device=DEV,
+                           dtype=torch.int32).to(torch.uint8)
+        vs = torch.randint(100, 160, (w.B, w.Hkv, nmax, w.Dv // 32), generator=g, device=DEV,
+                           dtype=torch.int32).to(torch.uint8)
+    cap = synth.capacity(ctx, w.P)
+    return synth.Inputs(w=w, seed=seed, ctx=list(ctx), cap=cap, q=torch.zeros(w.B, w.Hq, w.Dk, dtype=torch.bfloat16,
+                                                                                device=DEV),
+                        k=k, v=v, k_scale=ks, v_scale=vs)
+
+
+def _oracle_rows(inp, b, g):
+    """Oracle-decoded values of every token of (b, g) as float32 (bf16 by bits)."""
+    w = inp.w
+    n = inp.ctx[b]
+    if w.dtype == "bf16":
+        kb = inp.k[b, g, :n].cpu().view(torch.int16).numpy().view(np.uint16)
+        K = (kb.astype(np.uint32) << 16).view(np.float32)
+        V = None if w.v_alias_k else (inp.v[b, g, :n].cpu().view(torch.int16).numpy().view(np.uint16)
+                                      .astype(np.uint32) << 16).view(np.float32)
+        if w.v_alias_k:
+            V = K[:, :w.Dv]
+        return K, V
+    K, V = H.token_values(inp, b, g)
+    return K.astype(np.float32), V.astype(np.float32)
+
+
+def _check_placement(inp, cache):
+    w = inp.w
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            K, V = _oracle_rows(inp, b, g)
+            for r in range(w.P):
+                toks = opl.slice_tokens(inp.ctx[b], w.P, r)
+                if not toks:
+                    continue
+                ko = torch.empty(len(toks), w.Dk, dtype=torch.float32, device=DEV)
+                vo = torch.empty(len(toks), w.Dv, dtype=torch.float32, device=DEV)
+                api.kv_dequant(cache, r, b, g, 0, len(toks), ko, vo)
+                assert _same_f32(ko.cpu().numpy(), K[toks]), f"K rows of slice {r}, b={b}, g={g}"
+                assert _same_f32(vo.cpu().numpy(), V[toks]), f"V rows of slice {r}, b={b}, g={g}"
+
+
+PLACEMENT_CASES = [
+    configs.TINY_GQA.scaled(B=2, Hkv=2, Hq=4, ctx=None, ctx_range=(1, 300), P=3),
+    configs.FP8_GQA.scaled(B=3, Hkv=1, ctx=None, ctx_range=(1, 400), P=4),
+    configs.MXFP4_RAGGED.scaled(B=3, Hkv=2, Hq=4, ctx_range=(1, 500), P=8),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 200), P=2),
+]
+
+
+@pytest.mark.parametrize("w", PLACEMENT_CASES, ids=lambda w: w.dtype + ("-mla" if w.v_alias_k else ""))
+def test_append_places_bit_exact(w):
+    H.log(f"[placement] {w}")
+    ctx = synth.context_lengths(w, 11)
+    inp = _random_storage(w, ctx, seed=5)
+    cache = H.build_cache(inp)
+    _check_placement(inp, cache)
+
+
+@pytest.mark.parametrize("w", PLACEMENT_CASES[:3], ids=lambda w: w.dtype)
+def test_incremental_append_equals_bulk(w):
+    H.log(f"[incremental] {w}")
+    ctx = synth.context_lengths(w, 3)
+    inp = _random_storage(w, ctx, seed=9)
+    bulk = H.build_cache(inp)
+    desc = H.desc_of(inp)
+    inc = api.KVCache(desc, device=DEV, fill=0xFF)
+    rng = np.random.default_rng(0)
+    done = [0] * w.B
+    while any(d < n for d, n in zip(done, ctx)):
+        step = int(rng.integers(1, 40))
+        counts = [min(step, n - d) if rng.random() < 0.8 else 0 for d, n in zip(done, ctx)]
+        if sum(counts) == 0:
+            continue
+        sl = lambda t, b: t[b:b + 1, :, done[b]:done[b] + step] if t is not None else None
+        # one call per step; each request's rows start at its own position
+        kn = torch.stack([torch.nn.functional.pad(inp.k[b, :, done[b]:done[b] + counts[b]].view(torch.uint8),
+                                                  (0, 0, 0, step - counts[b])) for b in range(w.B)])
+        vn = None if inp.v is None else torch.stack(
+            [torch.nn.functional.pad(inp.v[b, :, done[b]:done[b] + counts[b]].view(torch.uint8),
+                                     (0, 0, 0, step - counts[b])) for b in range(w.B)])
+        if w.dtype == "bf16":
+            kn, vn = kn.view(torch.bfloat16), vn.view(torch.bfloat16)
+        ksn = vsn = None
+        if inp.k_scale is not None:
+            padfn = (lambda t, c: torch.nn.functional.pad(t, (0, step - c))) if w.dtype == "fp8_e4m3" else \
+                (lambda t, c: torch.nn.functional.pad(t, (0, 0, 0, step - c)))
+            ksn = torch.stack([padfn(inp.k_scale[b, :, done[b]:done[b] + counts[b]], counts[b]) for b in range(w.B)])
+            vsn = torch.stack([padfn(inp.v_scale[b, :, done[b]:done[b] + counts[b]], counts[b]) for b in range(w.B)])
+        api.kv_append(inc, kn.contiguous(), None if vn is None else vn.contiguous(),
+                      None if ksn is None else ksn.contiguous(), None if vsn is None else vsn.contiguous(),
+                      pos=done, count=counts)
+        done = [d + c for d, c in zip(done, counts)]
+        del sl
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a, b = getattr(bulk, name), getattr(inc, name)
+        if a is not None:
+            assert torch.equal(a, b), f"plane {name} differs"
+
+
+def test_fp8_every_code_dequantises_exactly():
+    w = configs.FP8_GQA.scaled(B=1, ctx=32, P=2)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(16).reshape(32, 128)
+    scales = torch.tensor([0.5] * 16 + [3.0] * 16, dtype=torch.float32)
+    inp = synth.Inputs(w=w, seed=0, ctx=[32], cap=16, q=torch.zeros(1, 16, 128, dtype=torch.bfloat16, device=DEV),
+                       k=codes[None, None].to(DEV), v=codes.flip(0)[None, None].contiguous().to(DEV),
+                       k_scale=scales[None, None].to(DEV), v_scale=(scales * 0.25)[None, None].to(DEV))
+    cache = H.build_cache(inp)
+    _check_placement(inp, cache)
+    # NaN codes decode to NaN; 0x7E is 448
+    assert np.isnan(ocod.FP8_E4M3[0x7F]) and ocod.FP8_E4M3[0x7E] == 448.0
+
+
+def test_mxfp4_every_code_and_exponent_dequantises_exactly():
+    w = configs.MXFP4_RAGGED.scaled(B=1, ctx=None, ctx_range=(48, 48), P=2)
+    pairs = torch.arange(256, dtype=torch.int32).to(torch.uint8)    # every (low, high) nibble pair
+    packed = pairs.repeat(48 * 64 // 256).reshape(48, 64)
+    exps = torch.tensor([1, 64, 120, 127, 134, 200, 254, 255], dtype=torch.int32).to(torch.uint8)
+    e8 = exps.repeat(48 * 4 // 8).reshape(48, 4)
+    inp = synth.Inputs(w=w, seed=0, ctx=[48], cap=32, q=torch.zeros(1, 16, 128, dtype=torch.bfloat16, device=DEV),
+                       k=packed[None, None].to(DEV), v=packed.flip(1)[None, None].contiguous().to(DEV),
+                       k_scale=e8[None, None].to(DEV), v_scale=e8.flip(0)[None, None].contiguous().to(DEV))
+    cache = H.build_cache(inp)
+    _check_placement(inp, cache)
+
+
+# ---------------------------------------------------------------- attention parity
+
+PARITY_CASES = [
+    configs.TINY_GQA,                                                                     # the tiny config itself
+    configs.TINY_GQA.scaled(B=3, Hkv=2, Hq=8, ctx=None, ctx_range=(1, 6000), P=4),        # GQA G=4, ragged
+    configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(1, 40000)),                  # G=16, P=8
+    configs.LLAMA405B_SHARE.scaled(B=3, ctx=None, ctx_range=(1, 50), P=2),                # tiny contexts
+    configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(100, 20000)),
+    configs.MXFP4_RAGGED.scaled(B=3, ctx_range=(1, 30000)),
+    configs.LLAMA405B_SHARE.scaled(B=2, Hq=2, ctx=None, ctx_range=(100, 9000), P=5),      # G=2
+    configs.TINY_GQA.scaled(B=1, Hq=1, ctx=3333, P=1),                                     # P=1, G=1
+]
+
+
+def _ids(w):
+    c = w.ctx if w.ctx is not None else f"{w.ctx_range[0]}-{w.ctx_range[1]}"
+    return f"{w.dtype}-B{w.B}-G{w.G}-Hkv{w.Hkv}-P{w.P}-n{c}"
+
+
+@pytest.mark.parametrize("needles", [False, True], ids=["plain", "needles"])
+@pytest.mark.parametrize("w", PARITY_CASES, ids=_ids)
+def test_decode_step_matches_oracle(w, needles):
+    seed = 1 + len(_ids(w))
+    H.log(f"[parity] {_ids(w)} needles={needles} seed={seed}")
+    inp = synth.make_inputs(w, seed, device=DEV, needles=needles)
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label=_ids(w))
+    H.log(f"   ctx={inp.ctx} worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
+def test_partials_are_deterministic_and_workspace_reusable():
+    w = configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(5000, 60000))
+    inp = synth.make_inputs(w, 4, device=DEV)
+    cache = H.build_cache(inp)
+    o1, l1, ws = H.run_partials(inp, cache)
+    # a different, smaller problem through the same workspace in between
+    w2 = configs.TINY_GQA.scaled(B=2, Hq=16, P=8, ctx=None, ctx_range=(1, 3000))
+    inp2 = synth.make_inputs(w2, 5, device=DEV)
+    cache2 = H.build_cache(inp2)
+    big = torch.zeros(max(ws.numel(), api.workspace_size(cache2.desc, w2.Hq)), dtype=torch.uint8, device=DEV)
+    a_o, a_l, _ = H.run_partials(inp, cache, big)
+    b_o, b_l, _ = H.run_partials(inp2, cache2, big)
+    c_o, c_l, _ = H.run_partials(inp, cache, big)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, a_o) and torch.equal(a_o, c_o)
+    assert torch.equal(l1, a_l) and torch.equal(a_l, c_l)
+    H.check_step(inp2, b_o, b_l, *H.run_combine(b_o, b_l), label="reused workspace")
+    H.check_step(inp, c_o, c_l, *H.run_combine(c_o, c_l), groups=[(0, 0)], label="after reuse")
+
+
+def test_decode_step_append_then_attend():
+    """The bench's step: the cache holds n-1 tokens, the step appends token
+    n-1 and attends over n; repeating the step is idempotent."""
+    w = configs.LLAMA405B_SHARE.scaled(B=3, ctx=None, ctx_range=(2, 20000))
+    inp = synth.make_inputs(w, 8, device=DEV, needles=True)
+    cache = H.build_cache(inp, upto=[n - 1 for n in inp.ctx])
+    last = [n - 1 for n in inp.ctx]
+    kn = torch.stack([inp.k[b, :, last[b]:last[b] + 1] for b in range(w.B)]).contiguous()
+    vn = torch.stack([inp.v[b, :, last[b]:last[b] + 1] for b in range(w.B)]).contiguous()
+    for _ in range(2):
+        api.kv_append(cache, kn, vn, None, None, pos=last)
+        o_part, lse_part, _ = H.run_partials(inp, cache)
+        o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    H.check_step(inp, o_part, lse_part, o, lse, label="append+attend")
+
+
+@pytest.mark.parametrize("P", [1, 3, 8, 100])
+def test_lse_combine_matches_oracle(P):
+    g = torch.Generator(device="cpu").manual_seed(P)
+    B, Hq, Dv = 3, 5, 128
+    o_part = torch.randn(P, B, Hq, Dv, generator=g)
+    lse_part = torch.randn(P, B, Hq, generator=g) * 20
+    empty = torch.rand(P, B, Hq, generator=g) < 0.3
+    lse_part[empty] = float("-inf")
+    o_part[empty] = 0.0
+    lse_part[:, 0, 0] = float("-inf")      # an all-empty row
+    o_part[:, 0, 0] = 0.0
+    o, lse = H.run_combine(o_part.to(DEV), lse_part.to(DEV))
+    O, L = oatt.combine(o_part.double().numpy(), lse_part.double().numpy())
+    torch.cuda.synchronize()
+    oc, lc = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lc), np.isneginf(L))
+    fin = ~np.isneginf(L)
+    assert np.max(np.abs(lc[fin] - L[fin]) / np.maximum(1, np.abs(L[fin]))) <= 1e-6
+    assert np.max(np.abs(oc - O)) <= 1e-5
+    assert np.all(oc[0, 0] == 0)
