@@ -30,6 +30,9 @@ COMMON = [
     "-Wno-unused-function",
     # packed fp32 VALU ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs, so the softmax rescale of
+    # the accumulator needs no AGPR round trips
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

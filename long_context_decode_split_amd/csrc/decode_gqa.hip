@@ -37,7 +37,14 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr float kLn2 = 0.693147180559945309f;
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// KV bytes are read exactly once: streaming (non-temporal) 16-byte loads, so
+// they do not evict what is reused (Q, partials) from the caches.
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -67,10 +74,11 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
 }
 
-// e8m0 -> fp32 2^(E-127) (E = 0 gives 2^-127, E = 255 gives NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return e == 0 ? __uint_as_float(0x00400000u) : (e == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e << 23));
-}
+// e8m0 byte -> fp32 2^(E-127) by placing E in the fp32 exponent field: one
+// shift, no branch.  Exact for E = 1..254; E = 0 (2^-127, elements below
+// 3.6e-38 in magnitude) reads as 0 and E = 255 (NaN) as +inf, so such blocks
+// give zero resp. non-finite contributions.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
 
 // Raw bytes of one chunk tile that a lane needs; FMT 0 bf16, 1 fp8, 2 MXFP4.
 template <int FMT>
@@ -116,6 +124,159 @@ struct Frag<2> {
   }
 };
 
+// Running state of one wave: O^T accumulator (lane l: heads l%16, value
+// columns 16*nb + 4*(l/16) + i), the running max of head l%16 in base-2
+// units (equal on the four lanes of a head), and this lane's shares of two
+// running sums: of the probabilities as rounded for the matrix cores (it
+// normalises O, keeping O a convex combination of V rows) and of the exact
+// probabilities (it gives the LSE).
+struct WaveState {
+  f32x4 acc[8];
+  float mrun;
+  float lsum_mfma;
+  float lsum;
+};
+
+// One 16-row chunk tile: scores, online softmax, O^T += V^T P^T.  TAIL marks
+// the last tile of a slice, whose rows at or past `valid` are masked (their
+// bytes may be anything, NaN included).
+template <int FMT, bool TAIL>
+__device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, const bf16x8 (&qf)[4], float c2,
+                                           int h, int valid) {
+  // ---- K fragments as bf16
+  bf16x8 kf[4];
+  float cscale = c2;
+  if constexpr (FMT == 0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
+  } else if constexpr (FMT == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w[4] = {cur.k[i].x, cur.k[i].y, cur.k[i].z, cur.k[i].w};
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {   // bytes 0-7 -> step 2i, 8-15 -> step 2i+1
+        uint4 t;
+        t.x = fp8x2_to_bf16x2<false>(w[2 * hs]);
+        t.y = fp8x2_to_bf16x2<true>(w[2 * hs]);
+        t.z = fp8x2_to_bf16x2<false>(w[2 * hs + 1]);
+        t.w = fp8x2_to_bf16x2<true>(w[2 * hs + 1]);
+        kf[2 * i + hs] = as_bf16x8(t);
+      }
+    }
+    cscale = c2 * cur.ks;
+  } else {
+    const uint32_t w[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float sc = e8m0_to_f32((cur.ksc >> (8 * s)) & 0xff);
+      uint4 t;
+      t.x = fp4x2_to_bf16x2<0>(w[s], sc);
+      t.y = fp4x2_to_bf16x2<1>(w[s], sc);
+      t.z = fp4x2_to_bf16x2<2>(w[s], sc);
+      t.w = fp4x2_to_bf16x2<3>(w[s], sc);
+      kf[s] = as_bf16x8(t);
+    }
+  }
+
+  // ---- scores: S^T[token 4h+i][head m]
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
+
+  uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;   // V halves of tokens 4h+{0,1} / 4h+{2,3}
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * h + i >= valid) sc[i] = -INFINITY;
+    keep01 = (4 * h + 0 < valid ? 0x0000ffffu : 0u) | (4 * h + 1 < valid ? 0xffff0000u : 0u);
+    keep23 = (4 * h + 2 < valid ? 0x0000ffffu : 0u) | (4 * h + 3 < valid ? 0xffff0000u : 0u);
+  }
+
+  // ---- online softmax (base 2)
+  float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  cm = fmaxf(cm, __shfl_xor(cm, 16));
+  cm = fmaxf(cm, __shfl_xor(cm, 32));
+  const float mnew = fmaxf(st.mrun, cm * cscale);
+  if (__builtin_amdgcn_ballot_w64(mnew > st.mrun)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[i] *= alpha;
+    st.lsum_mfma *= alpha;
+    st.lsum *= alpha;
+    st.mrun = mnew;
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -st.mrun));
+  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
+
+  // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
+  if constexpr (FMT == 0) {
+    const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+    st.lsum_mfma += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
+    const s16x4 pb = as_s16x4(p01, p23);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 vv = cur.v[i];
+      st.acc[2 * i] =
+          __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.x & keep01, vv.y & keep23), pb, st.acc[2 * i], 0, 0, 0);
+      st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.z & keep01, vv.w & keep23), pb,
+                                                                     st.acc[2 * i + 1], 0, 0, 0);
+    }
+  } else if constexpr (FMT == 1) {
+    // The tile's V scale is folded into P; the rounded products, divided by
+    // the scale, are what normalises O.
+    const float vsc = cur.vs;
+    const uint32_t p01 = pack_bf16(p[0] * vsc, p[1] * vsc), p23 = pack_bf16(p[2] * vsc, p[3] * vsc);
+    st.lsum_mfma += ((bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23))) * (1.0f / vsc);
+    const s16x4 pb = as_s16x4(p01, p23);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {   // value block nb = 4i + q: 4 codes (tokens 4h..4h+3)
+        const uint32_t lo = fp8x2_to_bf16x2<false>(w[q]) & keep01;
+        const uint32_t hi = fp8x2_to_bf16x2<true>(w[q]) & keep23;
+        st.acc[4 * i + q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo, hi), pb, st.acc[4 * i + q], 0, 0, 0);
+      }
+    }
+  } else {
+    // Per (token, 32-column block) scales are powers of two: fold them into
+    // P (exact), one P fragment per block.
+    const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+    const float pr[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
+    st.lsum_mfma += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const uint32_t vs[4] = {cur.vsc.x, cur.vsc.y, cur.vsc.z, cur.vsc.w};   // token 4h+j: 4 block scales
+    const uint32_t w[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      float ps[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ps[j] = pr[j] * e8m0_to_f32((vs[j] >> (8 * blk)) & 0xff);
+      if constexpr (TAIL) {   // rows past the slice end may hold any scale byte
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * h + j >= valid) ps[j] = 0.f;
+      }
+      const s16x4 pb = as_s16x4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]));
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int nb = 2 * blk + hb;   // bytes 2nb, 2nb+1 of the lane's 16 B
+        const uint32_t word = w[nb >> 1];
+        uint32_t lo, hi;
+        if ((nb & 1) == 0) {
+          lo = fp4x2_to_bf16x2<0>(word, 1.0f);
+          hi = fp4x2_to_bf16x2<1>(word, 1.0f);
+        } else {
+          lo = fp4x2_to_bf16x2<2>(word, 1.0f);
+          hi = fp4x2_to_bf16x2<3>(word, 1.0f);
+        }
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo & keep01, hi & keep23), pb, st.acc[nb], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs a) {
   const int lane = threadIdx.x & 63;
@@ -160,166 +321,68 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     }
   }
 
-  f32x4 acc[8];
+  WaveState st;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY;   // running max of head m, base-2 units; equal on the 4 lanes of a head
-  float lsum = 0.f;         // this lane's share of the running sum
+  for (int i = 0; i < 8; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.mrun = -INFINITY;
+  st.lsum_mfma = 0.f;
+  st.lsum = 0.f;
 
   const float c2 = a.c2;
-  Frag<FMT> nxt;
-  int c = c0 + wave;
-  if (c < c1) nxt.load(kp + (int64_t)c * a.k_tile, vp + (int64_t)c * a.v_tile, ksp ? ksp + (int64_t)c * a.ks_tile : nullptr,
-                       vsp ? vsp + (int64_t)c * a.vs_tile : nullptr, lane, 0);
-  for (; c < c1; c += kWaves) {
-    Frag<FMT> cur = nxt;
-    const int cn = c + kWaves;
-    if (cn < c1)
-      nxt.load(kp + (int64_t)cn * a.k_tile, vp + (int64_t)cn * a.v_tile, ksp ? ksp + (int64_t)cn * a.ks_tile : nullptr,
-               vsp ? vsp + (int64_t)cn * a.vs_tile : nullptr, lane, 0);
-
-    // ---- K fragments as bf16
-    bf16x8 kf[4];
-    float cscale = c2;
-    if constexpr (FMT == 0) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
-    } else if constexpr (FMT == 1) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t w[4] = {cur.k[i].x, cur.k[i].y, cur.k[i].z, cur.k[i].w};
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {   // bytes 0-7 -> step 2i, 8-15 -> step 2i+1
-          uint4 t;
-          t.x = fp8x2_to_bf16x2<false>(w[2 * hs]);
-          t.y = fp8x2_to_bf16x2<true>(w[2 * hs]);
-          t.z = fp8x2_to_bf16x2<false>(w[2 * hs + 1]);
-          t.w = fp8x2_to_bf16x2<true>(w[2 * hs + 1]);
-          kf[2 * i + hs] = as_bf16x8(t);
-        }
-      }
-      cscale = c2 * cur.ks;
-    } else {
-      const uint32_t w[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float sc = e8m0_to_f32((cur.ksc >> (8 * s)) & 0xff);
-        uint4 t;
-        t.x = fp4x2_to_bf16x2<0>(w[s], sc);
-        t.y = fp4x2_to_bf16x2<1>(w[s], sc);
-        t.z = fp4x2_to_bf16x2<2>(w[s], sc);
-        t.w = fp4x2_to_bf16x2<3>(w[s], sc);
-        kf[s] = as_bf16x8(t);
-      }
+  auto load = [&](Frag<FMT>& f, int c) {
+    f.load(kp + (int64_t)c * a.k_tile, vp + (int64_t)c * a.v_tile, ksp ? ksp + (int64_t)c * a.ks_tile : nullptr,
+           vsp ? vsp + (int64_t)c * a.vs_tile : nullptr, lane, 0);
+  };
+  auto step = [&](const Frag<FMT>& f, int c) {
+    if (c == nch - 1 && tail_valid < kChunk)
+      chunk_step<FMT, true>(f, st, qf, c2, h, tail_valid);
+    else
+      chunk_step<FMT, false>(f, st, qf, c2, h, kChunk);
+  };
+  // Two tiles in flight per wave: while one is consumed the other is loading,
+  // and each reload goes straight into the registers just consumed.  The
+  // steady-state loop issues its loads unconditionally so the wait counts
+  // stay exact (the wave keeps the other tile's loads in flight while it
+  // computes); the last two or three tiles are drained after it.
+  const int first = c0 + wave;
+  const int nmine = __builtin_amdgcn_readfirstlane(first < c1 ? (c1 - first + kWaves - 1) / kWaves : 0);
+  if (nmine > 0) {
+    auto chunk = [&](int i) { return first + i * kWaves; };
+    Frag<FMT> fa, fb;
+    load(fa, chunk(0));
+    load(fb, chunk(nmine > 1 ? 1 : 0));
+    int i = 0;
+    for (; i + 3 < nmine; i += 2) {
+      step(fa, chunk(i));
+      load(fa, chunk(i + 2));
+      step(fb, chunk(i + 1));
+      load(fb, chunk(i + 3));
     }
-
-    // ---- scores: S^T[token 4h+i][head m]
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
-
-    const bool tail = (c == nch - 1) && (tail_valid < kChunk);
-    uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;   // V halves of tokens 4h+{0,1} / 4h+{2,3}
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * h + i >= tail_valid) sc[i] = -INFINITY;
-      keep01 = (4 * h + 0 < tail_valid ? 0x0000ffffu : 0u) | (4 * h + 1 < tail_valid ? 0xffff0000u : 0u);
-      keep23 = (4 * h + 2 < tail_valid ? 0x0000ffffu : 0u) | (4 * h + 3 < tail_valid ? 0xffff0000u : 0u);
-    }
-
-    // ---- online softmax (base 2)
-    float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    const float mnew = fmaxf(mrun, cm * cscale);
-    if (__builtin_amdgcn_ballot_w64(mnew > mrun)) {
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-      lsum *= alpha;
-      mrun = mnew;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -mrun));
-
-    // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
-    if constexpr (FMT == 0) {
-      const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-      lsum += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
-      const s16x4 pb = as_s16x4(p01, p23);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 vv = cur.v[i];
-        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.x & keep01, vv.y & keep23), pb, acc[2 * i], 0, 0, 0);
-        acc[2 * i + 1] =
-            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.z & keep01, vv.w & keep23), pb, acc[2 * i + 1], 0, 0, 0);
-      }
-    } else if constexpr (FMT == 1) {
-      // V scale of the tile folded into P; the sum uses the rounded values.
-      const float vsc = cur.vs;
-      const uint32_t p01 = pack_bf16(p[0] * vsc, p[1] * vsc), p23 = pack_bf16(p[2] * vsc, p[3] * vsc);
-      lsum += ((bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23))) * (1.0f / vsc);
-      const s16x4 pb = as_s16x4(p01, p23);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t w[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {   // column block nb = 4i + q: 4 codes (tokens 4h..4h+3)
-          const uint32_t lo = fp8x2_to_bf16x2<false>(w[q]) & keep01;
-          const uint32_t hi = fp8x2_to_bf16x2<true>(w[q]) & keep23;
-          acc[4 * i + q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo, hi), pb, acc[4 * i + q], 0, 0, 0);
-        }
-      }
-    } else {
-      // Per (token, 32-column block) scales are powers of two: fold them into
-      // P (exact), one P fragment per block; the sum uses unscaled rounded P.
-      const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-      lsum += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
-      const float pr[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
-      const uint32_t vs[4] = {cur.vsc.x, cur.vsc.y, cur.vsc.z, cur.vsc.w};   // token 4h+j: 4 block scales
-      const uint32_t w[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        float ps[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ps[j] = pr[j] * e8m0_to_f32((vs[j] >> (8 * blk)) & 0xff);
-        if (tail) {   // rows past the slice end may hold any scale byte, NaN included
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * h + j >= tail_valid) ps[j] = 0.f;
-        }
-        const s16x4 pb = as_s16x4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]));
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int nb = 2 * blk + hb;   // bytes 2nb, 2nb+1 of the lane's 16 B
-          const uint32_t word = w[nb >> 1];
-          uint32_t lo, hi;
-          if ((nb & 1) == 0) {
-            lo = fp4x2_to_bf16x2<0>(word, 1.0f);
-            hi = fp4x2_to_bf16x2<1>(word, 1.0f);
-          } else {
-            lo = fp4x2_to_bf16x2<2>(word, 1.0f);
-            hi = fp4x2_to_bf16x2<3>(word, 1.0f);
-          }
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo & keep01, hi & keep23), pb, acc[nb], 0, 0, 0);
-        }
-      }
-    }
+    if (i < nmine) step(fa, chunk(i));
+    if (i + 2 < nmine) load(fa, chunk(i + 2));
+    if (i + 1 < nmine) step(fb, chunk(i + 1));
+    if (i + 2 < nmine) step(fa, chunk(i + 2));
   }
+  float mrun = st.mrun, lsum = st.lsum, lsum_mfma = st.lsum_mfma;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = st.acc[i];
 
   // ---- fold the lanes' running sums of each head
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+  lsum_mfma += __shfl_xor(lsum_mfma, 16);
+  lsum_mfma += __shfl_xor(lsum_mfma, 32);
 
   // ---- combine the waves of this workgroup (LSE rule, base 2)
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
+  __shared__ float s_lm[kWaves][16];
   __shared__ float s_acc[kWaves][16][kD + 4];
   if (h == 0) {
     s_m[wave][m] = mrun;
     s_l[wave][m] = lsum;
+    s_lm[wave][m] = lsum_mfma;
   }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
@@ -344,16 +407,17 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     float M = s_m[0][hd];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hd]);
-    float num = 0.f, den = 0.f;
+    float num = 0.f, den = 0.f, den_mfma = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float f = __builtin_amdgcn_exp2f(s_m[w][hd] - M);
         num += f * s_acc[w][hd][dv];
         den += f * s_l[w][hd];
+        den_mfma += f * s_lm[w][hd];
       }
     }
-    out_o[hd * ostride_head + dv] = den > 0.f ? num / den : 0.f;
+    out_o[hd * ostride_head + dv] = den_mfma > 0.f ? num / den_mfma : 0.f;
     if (dv == 0) out_l[hd] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
   }
   if (direct) return;
@@ -367,22 +431,51 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
   __syncthreads();
   if (!s_last) return;
   __threadfence();
+  // Split weights in LDS (the wave-combine buffer is free again): first the
+  // LSEs of all splits, then per head the max and the weights.  The partial
+  // outputs are then read with every split's load of a thread in flight at
+  // once, so the fold costs a few memory round trips.
   const int rec0 = wg - split;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int hd = idx / kD, dv = idx % kD;
+  float* s_w = &s_acc[0][0][0];                 // [nsplit][G]
+  __shared__ float s_fm[16], s_fden[16];
+  for (int i = threadIdx.x; i < nsplit * G; i += kThreads) s_w[i] = a.ws_lse[(int64_t)rec0 * G + i];
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hd = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(a.ws_lse + (int64_t)(rec0 + s) * G + hd));
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float l = __builtin_nontemporal_load(a.ws_lse + (int64_t)(rec0 + s) * G + hd);
-        const float f = __builtin_amdgcn_exp2f((l - M) * 1.44269504088896341f);
-        num += f * __builtin_nontemporal_load(a.ws_o + ((int64_t)(rec0 + s) * G + hd) * a.Dv + dv);
-        den += f;
-      }
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, s_w[s * G + hd]);
+    float den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((s_w[s * G + hd] - M) * 1.44269504088896341f);
+      s_w[s * G + hd] = wgt;
+      den += wgt;
     }
-    a.o_part[(((int64_t)r * a.Btot + b) * a.Hq + g * G + hd) * a.Dv + dv] = den > 0.f ? num / den : 0.f;
-    if (dv == 0) a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + hd] = den > 0.f ? M + __log2f(den) * kLn2 : -INFINITY;
+    s_fm[hd] = M;
+    s_fden[hd] = den;
+  }
+  __syncthreads();
+  const int nq = G * kD / 4;   // float4 outputs of this slice
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_o + (int64_t)rec0 * G * kD);
+  f32x4* dst = reinterpret_cast<f32x4*>(a.o_part + (((int64_t)r * a.Btot + b) * a.Hq + g * G) * kD);
+  for (int qi = threadIdx.x; qi < nq; qi += kThreads) {
+    const int hd = qi / (kD / 4);
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * nq + qi];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) num += s_w[(s + u) * G + hd] * v[u];
+    }
+    for (; s < nsplit; ++s) num += s_w[s * G + hd] * src[(int64_t)s * nq + qi];
+    const float den = s_fden[hd];
+    dst[qi] = den > 0.f ? num * (1.0f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (threadIdx.x < G) {
+    const float den = s_fden[threadIdx.x];
+    a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + threadIdx.x] =
+        den > 0.f ? s_fm[threadIdx.x] + __log2f(den) * kLn2 : -INFINITY;
   }
   if (threadIdx.x == 0) *ctr = 0u;
 }

@@ -383,7 +383,10 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
       nch[i] = (slice_len(a.n[i], d.P, 0) + kChunk - 1) / kChunk;   // slice 0 is never shorter
       W += nch[i] * d.Hkv * d.P;
     }
+    int64_t nch_max = 1;
+    for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
     int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
+    cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
     a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
     int wgs = 0;
     for (int i = 0; i < nb; ++i) {

@@ -222,6 +222,7 @@ hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part,
 constexpr int kGqaWavesPerWg = 4;
 constexpr int kGqaTargetWgs = 2048;   // upper bound on the split target
 constexpr int kMlaTargetWgs = 1024;
+constexpr int kMaxSplits = 256;       // splits per slice (the fold keeps their weights in LDS)
 int target_wgs(int kind);            // device-dependent, <= the bounds above
 int min_chunks_per_wg(int kind);
 

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   const int64_t end = pos + a.count[bl];
   const int64_t c = pos / kChunk + ci;           // request-level chunk (group) index
   const int64_t row0 = c * kChunk;
-  if (row0 >= end) return;
+  if (end == pos || row0 >= end) return;   // nothing of this request lands in this chunk
   const int r = (int)(c % a.P);
   const int64_t lc = c / a.P;
   const int64_t tile = ((int64_t)(r * a.B + b) * a.Hkv + g) * a.cap_chunks + lc;
