@@ -160,12 +160,13 @@ hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_
                         int64_t j0, int64_t n, float* k_out, float* v_out, void* stream);
 
 /* Workspace bytes hx_decode_attn_partial needs for `desc` with Hq query
- * heads (host only).  The workspace must be zero-filled before its first
- * use (hx_workspace_init does that); every call leaves its counters at zero
- * again, so one workspace serves any number of calls on one stream. */
+ * heads (host only).  The workspace holds the partial results of the splits
+ * each slice is cut into; it needs no initialisation and its contents are
+ * scratch between calls. */
 hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes);
 
-/* Zero a workspace (device) on `stream`. */
+/* Zero a workspace (device) on `stream` (optional; for callers that want
+ * deterministic bytes in it). */
 hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Per-slice partial attention for one decode step, every slice in one
@@ -181,6 +182,8 @@ hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   lse_part device float [P][B][Hq]: LSE_r = ln sum_{t in r} exp(s_t)
  *            (natural log); -inf for an empty slice.
  *   ws       device workspace of hx_workspace_size bytes (see there).
+ * A call launches the partial kernel and, when some slice is cut into
+ * several splits, a small kernel that folds the splits of each slice.
  * Calls that share a workspace must be ordered (same stream). */
 hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
                                  const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,

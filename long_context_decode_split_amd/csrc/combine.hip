@@ -57,7 +57,77 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(int P, int rows, 
   if (tid == 0) lse[row] = den > 0.f ? m + __log2f(den) * kLn2 : -INFINITY;
 }
 
+// Fold of the split records of one slice into the slice's partial, by the
+// same LSE rule: one workgroup per (slice, query head), threads over value
+// columns.  The split LSEs and weights live in LDS; each thread keeps eight
+// splits' loads in flight at a time.
+constexpr int kFoldThreads = 128;
+
+__global__ __launch_bounds__(kFoldThreads) void split_fold_kernel(const PartialArgs a) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kFoldThreads / 64];
+  const int G = a.G, Dv = a.Dv, P = a.P;
+  const int f = blockIdx.x;
+  int bl = 0;
+  while (bl + 1 < a.nb && a.fold_begin[bl + 1] <= f) ++bl;
+  const int nsplit = a.nsplit[bl];
+  int rem = f - a.fold_begin[bl];
+  const int hd = rem % G;
+  rem /= G;
+  const int r = rem % P;
+  const int g = rem / P;
+  const int b = a.b0 + bl;
+  const int64_t rec0 = a.wg_begin[bl] + (int64_t)(g * P + r) * nsplit;
+  const int tid = threadIdx.x;
+
+  float m = -INFINITY;
+  for (int sp = tid; sp < nsplit; sp += kFoldThreads) {
+    const float l = a.ws_lse[(rec0 + sp) * G + hd];
+    s_w[sp] = l;
+    m = fmaxf(m, l);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kFoldThreads / 64; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+  const bool empty = m == -INFINITY;
+  for (int sp = tid; sp < nsplit; sp += kFoldThreads)
+    s_w[sp] = empty ? 0.f : __builtin_amdgcn_exp2f((s_w[sp] - m) * kLog2e);
+  __syncthreads();
+  float den = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) den += s_w[sp];
+
+  const float* src = a.ws_o + (rec0 * G + hd) * (int64_t)Dv;
+  const int64_t rstride = (int64_t)G * Dv;   // floats between split records
+  float* dst = a.o_part + (((int64_t)r * a.Btot + b) * a.Hq + g * G + hd) * Dv;
+  for (int d = tid; d < Dv; d += kFoldThreads) {
+    float num = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= nsplit; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(sp + u) * rstride + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) num += s_w[sp + u] * v[u];
+    }
+    for (; sp < nsplit; ++sp) num += s_w[sp] * src[sp * rstride + d];
+    dst[d] = den > 0.f ? num / den : 0.f;
+  }
+  if (tid == 0)
+    a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + hd] = den > 0.f ? m + __log2f(den) * kLn2 : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_split_fold(const PartialArgs& a, hipStream_t st) {
+  const int nf = a.fold_begin[a.nb];
+  if (nf == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_fold_kernel, dim3(nf), dim3(kFoldThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part, const float* lse_part, float* o,
                               float* lse, hipStream_t st) {

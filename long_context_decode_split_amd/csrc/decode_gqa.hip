@@ -5,9 +5,13 @@
 // every request b, KV head g and slice r, the partial attention of the G
 // query heads of g over the rows of slice r, as a normalised output and a
 // natural-log LSE.  The rows of a slice are cut into splits of `cpw` 16-row
-// chunk tiles so the launch fills the GPU; each workgroup streams one split,
-// and the last workgroup of a slice to finish folds the splits of that slice
-// with the LSE combine (jaehun.me review, Prompt 1.3.2).
+// chunk tiles so the launch fills the GPU; each workgroup streams one split
+// and writes its partial (straight into the slice's output when the slice has
+// a single split).  A second, small kernel folds the splits of each slice with
+// the LSE combine (jaehun.me review, Prompt 1.3.2): the kernel boundary makes
+// the records visible, where an in-kernel last-workgroup fold would need a
+// device-scope release and acquire per workgroup (an L2 write-back and
+// invalidate each), which measured at about 15% of the kernel time.
 //
 // Work per wave, per 16-row chunk tile (no LDS on the streaming path):
 //   * 4 x 16 B loads of K and 4 x 16 B loads of V (bf16; fewer for fp8 and
@@ -33,6 +37,16 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kWaves = kGqaWavesPerWg;
+
+// Chunk tiles a wave keeps in flight (register budget: 32 VGPRs per bf16 tile).
+#ifndef HX_GQA_TILES_BF16
+#define HX_GQA_TILES_BF16 2
+#endif
+#ifndef HX_GQA_TILES_Q
+#define HX_GQA_TILES_Q 3
+#endif
+template <int FMT>
+constexpr int kTilesInFlight = FMT == 0 ? HX_GQA_TILES_BF16 : HX_GQA_TILES_Q;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr float kLn2 = 0.693147180559945309f;
@@ -196,15 +210,15 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   cm = fmaxf(cm, __shfl_xor(cm, 16));
   cm = fmaxf(cm, __shfl_xor(cm, 32));
+  // Rescale unconditionally (alpha = 1 when the max did not grow): a branch
+  // here would cost more in register copies than the 32 multiplies.
   const float mnew = fmaxf(st.mrun, cm * cscale);
-  if (__builtin_amdgcn_ballot_w64(mnew > st.mrun)) {
-    const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
+  const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[i] *= alpha;
-    st.lsum_mfma *= alpha;
-    st.lsum *= alpha;
-    st.mrun = mnew;
-  }
+  for (int i = 0; i < 8; ++i) st.acc[i] *= alpha;
+  st.lsum_mfma *= alpha;
+  st.lsum *= alpha;
+  st.mrun = mnew;
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -st.mrun));
@@ -333,35 +347,50 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     f.load(kp + (int64_t)c * a.k_tile, vp + (int64_t)c * a.v_tile, ksp ? ksp + (int64_t)c * a.ks_tile : nullptr,
            vsp ? vsp + (int64_t)c * a.vs_tile : nullptr, lane, 0);
   };
-  auto step = [&](const Frag<FMT>& f, int c) {
-    if (c == nch - 1 && tail_valid < kChunk)
-      chunk_step<FMT, true>(f, st, qf, c2, h, tail_valid);
-    else
-      chunk_step<FMT, false>(f, st, qf, c2, h, kChunk);
-  };
-  // Two tiles in flight per wave: while one is consumed the other is loading,
-  // and each reload goes straight into the registers just consumed.  The
-  // steady-state loop issues its loads unconditionally so the wait counts
-  // stay exact (the wave keeps the other tile's loads in flight while it
-  // computes); the last two or three tiles are drained after it.
+  // The slice's partial last tile (if this split holds it) is taken out of
+  // the streaming loop and done once at the end, so the loop has no branch.
+  const bool has_tail = c1 == nch && c1 > c0 && tail_valid < kChunk;
+  const int c1f = has_tail ? c1 - 1 : c1;
+
+  // NBUF tiles in flight per wave: each reload goes straight into the
+  // registers of the tile just consumed.  The steady-state loop issues its
+  // loads unconditionally so the wait counts stay exact (the wave keeps the
+  // other tiles' loads in flight while it computes); the last tiles are
+  // drained after it.
+  constexpr int NBUF = kTilesInFlight<FMT>;
   const int first = c0 + wave;
-  const int nmine = __builtin_amdgcn_readfirstlane(first < c1 ? (c1 - first + kWaves - 1) / kWaves : 0);
+  const int nmine = __builtin_amdgcn_readfirstlane(first < c1f ? (c1f - first + kWaves - 1) / kWaves : 0);
   if (nmine > 0) {
     auto chunk = [&](int i) { return first + i * kWaves; };
-    Frag<FMT> fa, fb;
-    load(fa, chunk(0));
-    load(fb, chunk(nmine > 1 ? 1 : 0));
+    Frag<FMT> f[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) load(f[k], chunk(k < nmine ? k : nmine - 1));
     int i = 0;
-    for (; i + 3 < nmine; i += 2) {
-      step(fa, chunk(i));
-      load(fa, chunk(i + 2));
-      step(fb, chunk(i + 1));
-      load(fb, chunk(i + 3));
+    for (; i + 2 * NBUF - 1 < nmine; i += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
+        load(f[k], chunk(i + k + NBUF));
+#if HX_GQA_SCHED_BARRIER
+        __builtin_amdgcn_sched_barrier(0);   // keep the next tile's math below this reload
+#endif
+      }
     }
-    if (i < nmine) step(fa, chunk(i));
-    if (i + 2 < nmine) load(fa, chunk(i + 2));
-    if (i + 1 < nmine) step(fb, chunk(i + 1));
-    if (i + 2 < nmine) step(fa, chunk(i + 2));
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) {
+      if (i + k < nmine) {
+        chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
+        if (i + k + NBUF < nmine) load(f[k], chunk(i + k + NBUF));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k)
+      if (i + NBUF + k < nmine) chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
+  }
+  if (has_tail && wave == (c1 - 1 - c0) % kWaves) {
+    Frag<FMT> t;
+    load(t, c1 - 1);
+    chunk_step<FMT, true>(t, st, qf, c2, h, tail_valid);
   }
   float mrun = st.mrun, lsum = st.lsum, lsum_mfma = st.lsum_mfma;
   f32x4 acc[8];
@@ -420,64 +449,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     out_o[hd * ostride_head + dv] = den_mfma > 0.f ? num / den_mfma : 0.f;
     if (dv == 0) out_l[hd] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
   }
-  if (direct) return;
 
-  // ---- the last workgroup of this slice folds the splits
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  unsigned* ctr = a.counters + ((int64_t)b * a.Hkv + g) * a.P + r;
-  if (threadIdx.x == 0) s_last = (atomicAdd(ctr, 1u) == (unsigned)(nsplit - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // Split weights in LDS (the wave-combine buffer is free again): first the
-  // LSEs of all splits, then per head the max and the weights.  The partial
-  // outputs are then read with every split's load of a thread in flight at
-  // once, so the fold costs a few memory round trips.
-  const int rec0 = wg - split;
-  float* s_w = &s_acc[0][0][0];                 // [nsplit][G]
-  __shared__ float s_fm[16], s_fden[16];
-  for (int i = threadIdx.x; i < nsplit * G; i += kThreads) s_w[i] = a.ws_lse[(int64_t)rec0 * G + i];
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int hd = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, s_w[s * G + hd]);
-    float den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float wgt = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((s_w[s * G + hd] - M) * 1.44269504088896341f);
-      s_w[s * G + hd] = wgt;
-      den += wgt;
-    }
-    s_fm[hd] = M;
-    s_fden[hd] = den;
-  }
-  __syncthreads();
-  const int nq = G * kD / 4;   // float4 outputs of this slice
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_o + (int64_t)rec0 * G * kD);
-  f32x4* dst = reinterpret_cast<f32x4*>(a.o_part + (((int64_t)r * a.Btot + b) * a.Hq + g * G) * kD);
-  for (int qi = threadIdx.x; qi < nq; qi += kThreads) {
-    const int hd = qi / (kD / 4);
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
-      f32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * nq + qi];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) num += s_w[(s + u) * G + hd] * v[u];
-    }
-    for (; s < nsplit; ++s) num += s_w[s * G + hd] * src[(int64_t)s * nq + qi];
-    const float den = s_fden[hd];
-    dst[qi] = den > 0.f ? num * (1.0f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (threadIdx.x < G) {
-    const float den = s_fden[threadIdx.x];
-    a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + threadIdx.x] =
-        den > 0.f ? s_fm[threadIdx.x] + __log2f(den) * kLn2 : -INFINITY;
-  }
-  if (threadIdx.x == 0) *ctr = 0u;
 }
 
 }  // namespace

@@ -89,9 +89,13 @@ static int device_cus() {
   return cache[dev];
 }
 
-int target_wgs(int kind) {
-  // Workgroups per CU for one launch; HX_WGS_PER_CU overrides (tuning knob).
-  const int per_cu = env_int("HX_WGS_PER_CU", kind == 0 ? 4 : 2, 1, 8);
+int target_wgs(int kind, int dtype) {
+  // Workgroups per CU for one launch, measured on MI355X at 1M-token contexts:
+  // bf16 / fp8 tiles stream best with two workgroups per CU (one round, all
+  // resident); MXFP4 tiles carry more dequantisation work per byte and gain
+  // from more waves.  HX_WGS_PER_CU overrides (tuning knob).
+  const int dflt = kind != 0 ? 2 : (dtype == HX_KV_MXFP4 ? 4 : 2);
+  const int per_cu = env_int("HX_WGS_PER_CU", dflt, 1, 8);
   const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
   return std::min(bound, device_cus() * per_cu);
 }
@@ -105,16 +109,17 @@ static int64_t ws_records(const hx_kv_desc& d, int kind) {
 
 static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
+// Workspace: one record per workgroup of a launch, [records][G][Dv] partial
+// outputs then [records][G] LSEs.
 struct WsLayout {
-  int64_t counters_off, o_off, lse_off, total;
+  int64_t o_off, lse_off, total;
 };
 
 static WsLayout ws_layout(const hx_kv_desc& d, int kind, int G) {
   WsLayout w;
   const int64_t recs = ws_records(d, kind);
-  w.counters_off = 0;
-  w.o_off = align256((int64_t)d.B * d.Hkv * d.P * 4);
-  w.lse_off = w.o_off + align256(recs * G * d.Dv * 4);
+  w.o_off = 0;
+  w.lse_off = align256(recs * G * d.Dv * 4);
   w.total = w.lse_off + align256(recs * G * 4);
   return w;
 }
@@ -355,7 +360,6 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
   a.q = (const uint16_t*)q;
   a.o_part = o_part;
   a.lse_part = lse_part;
-  a.counters = (unsigned*)((uint8_t*)ws + wl.counters_off);
   a.ws_o = (float*)((uint8_t*)ws + wl.o_off);
   a.ws_lse = (float*)((uint8_t*)ws + wl.lse_off);
   a.P = d.P;
@@ -372,7 +376,7 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
   a.vs_tile = d.v_alias_k ? geo.ks_tile : geo.vs_tile;
   a.c2 = scale * 1.44269504088896341f;
   const int64_t records = ws_records(d, geo.kind);
-  const int target = target_wgs(geo.kind);
+  const int target = target_wgs(geo.kind, d.dtype);
   const int minc = min_chunks_per_wg(geo.kind);
   for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
@@ -388,19 +392,24 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
     int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
     cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
     a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
-    int wgs = 0;
+    int wgs = 0, folds = 0;
     for (int i = 0; i < nb; ++i) {
       a.nsplit[i] = (int)((nch[i] + a.cpw - 1) / a.cpw);
       a.wg_begin[i] = wgs;
+      a.fold_begin[i] = folds;
       wgs += a.nsplit[i] * d.Hkv * d.P;
+      if (a.nsplit[i] > 1) folds += d.Hkv * d.P * G;
     }
     a.wg_begin[nb] = wgs;
+    a.fold_begin[nb] = folds;
     if (wgs > records) return fail(HX_EINVAL, "internal: %d workgroups exceed the %lld workspace records", wgs, (long long)records);
     a.b0 = b0;
     a.nb = nb;
     hipError_t e = geo.kind == 0 ? launch_gqa_partial(a, d.dtype, (hipStream_t)stream)
                                  : launch_mla_partial(a, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
+    if (s) return s;
+    s = check_hip(launch_split_fold(a, (hipStream_t)stream), "split fold launch");
     if (s) return s;
   }
   return HX_OK;

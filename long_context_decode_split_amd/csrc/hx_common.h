@@ -202,7 +202,6 @@ struct PartialArgs {
   float* lse_part;         // [P][Btot][Hq]
   float* ws_o;             // [records][G][Dv]
   float* ws_lse;           // [records][G]
-  unsigned* counters;      // [Btot][Hkv][P]
   int P, Btot, b0, nb, Hkv, Hq, G, Dk, Dv;
   int64_t cap_chunks;
   int64_t k_tile, v_tile, ks_tile, vs_tile;
@@ -210,10 +209,14 @@ struct PartialArgs {
   int cpw;                 // chunks per workgroup (split size)
   int64_t n[kMaxBatchPerLaunch];
   int nsplit[kMaxBatchPerLaunch];
-  int wg_begin[kMaxBatchPerLaunch + 1];
+  int wg_begin[kMaxBatchPerLaunch + 1];     // first workgroup (= split record) of each request
+  int fold_begin[kMaxBatchPerLaunch + 1];   // first fold workgroup of each request
 };
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
 hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
+// Folds the split records of every slice with more than one split into the
+// slice outputs (o_part, lse_part); no-op when every slice has one split.
+hipError_t launch_split_fold(const PartialArgs& a, hipStream_t st);
 
 hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part, const float* lse_part, float* o,
                               float* lse, hipStream_t st);
@@ -223,7 +226,7 @@ constexpr int kGqaWavesPerWg = 4;
 constexpr int kGqaTargetWgs = 2048;   // upper bound on the split target
 constexpr int kMlaTargetWgs = 1024;
 constexpr int kMaxSplits = 256;       // splits per slice (the fold keeps their weights in LDS)
-int target_wgs(int kind);            // device-dependent, <= the bounds above
+int target_wgs(int kind, int dtype);  // device-dependent, <= the bounds above
 int min_chunks_per_wg(int kind);
 
 }  // namespace hx
