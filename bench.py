@@ -55,6 +55,34 @@ def setup(w, seed):
     return inp, cache, step_in, ws, o_part, lse_part, o, lse
 
 
+def kernel_src_hash():
+    """Hash of the GQA kernel sources, to tell whether recorded counters
+    still describe the kernel that runs."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for p in ("decode_gqa.hip", "hx_common.h"):
+        with open(os.path.join(here, "long_context_decode_split_amd", "csrc", p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the partial kernel from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json (scaled by
+    a copy of known size), or None when none was recorded for this workload
+    or the kernel sources changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_src_sha16") != kernel_src_hash():
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+
+
 def cpu_baseline(inp, budget_s=20.0):
     """The oracle (fp64, numpy) on a bounded sample of the same step: whole
     (request, KV head) groups over their full context, as many as fit the
@@ -113,7 +141,18 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (5 times); used to scale the "
+                         "HBM traffic counters of a profiler run")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "copies": 5}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -194,7 +233,7 @@ def main():
             "peak": peak_gbs,
             "unit": "GB/s",
             "frac": round(kern_gbs / peak_gbs, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(w.name),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
         },
