@@ -30,12 +30,17 @@ COMMON = [
     "-Wno-unused-function",
     # packed fp32 VALU ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core accumulators in ordinary VGPRs, so the softmax rescale of
-    # the accumulator needs no AGPR round trips
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
+
+
+# Per-source extra flags.  The GQA kernel keeps its matrix-core accumulators
+# in ordinary VGPRs (the softmax rescale then needs no AGPR round trips); the
+# MLA kernel needs the AGPRs for its 256-register accumulator.
+EXTRA = {
+    "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc():
@@ -47,7 +52,7 @@ def hipcc():
 
 def _compile(src, cc, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [cc, *COMMON, "-c", src, "-o", obj]
+    cmd = [cc, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

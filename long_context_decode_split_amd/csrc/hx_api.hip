@@ -54,7 +54,7 @@ hx_status geometry(const hx_kv_desc& d, Geometry* g) {
     }
   } else if (d.Dk == 576 && d.Dv == 512 && d.v_alias_k && d.dtype == HX_KV_BF16) {
     t.kind = 1;
-    t.lay_k = kLayRowBf16; t.lay_v = -1; t.ebits = 16;
+    t.lay_k = kLayMlaBf16; t.lay_v = -1; t.ebits = 16;
     t.k_tile = (int64_t)kChunk * 576 * 2; t.v_tile = 0; t.ks_tile = t.vs_tile = 0;
   } else {
     return fail(HX_EUNSUPPORTED, "unsupported cache: Dk=%d Dv=%d v_alias_k=%d dtype=%d", d.Dk, d.Dv, d.v_alias_k,
@@ -93,8 +93,9 @@ int target_wgs(int kind, int dtype) {
   // Workgroups per CU for one launch, measured on MI355X at 1M-token contexts:
   // bf16 / fp8 tiles stream best with two workgroups per CU (one round, all
   // resident); MXFP4 tiles carry more dequantisation work per byte and gain
-  // from more waves.  HX_WGS_PER_CU overrides (tuning knob).
-  const int dflt = kind != 0 ? 2 : (dtype == HX_KV_MXFP4 ? 4 : 2);
+  // from more waves.  The MLA kernel holds 152 KiB of LDS: one workgroup of
+  // eight waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
+  const int dflt = kind != 0 ? 1 : (dtype == HX_KV_MXFP4 ? 4 : 2);
   const int per_cu = env_int("HX_WGS_PER_CU", dflt, 1, 8);
   const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
   return std::min(bound, device_cus() * per_cu);
@@ -391,6 +392,7 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
     for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
     int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
     cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
+    if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
     a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
     int wgs = 0, folds = 0;
     for (int i = 0; i < nb; ++i) {

@@ -43,9 +43,16 @@ enum Layout : int {
   kLayGqaBf16K = 0, kLayGqaBf16V = 1,
   kLayGqaFp8K = 2, kLayGqaFp8V = 3,
   kLayGqaFp4K = 4, kLayGqaFp4V = 5,
-  kLayRowBf16 = 6,   // plain row-major bf16 rows (MLA latent rows)
+  kLayMlaBf16 = 6,   // bf16 latent rows, 16-byte pieces XOR-swizzled inside each aligned group of 8
   kLayRowU8 = 7,     // plain row-major bytes (MXFP4 e8m0 scale rows)
 };
+
+// MLA latent rows (1152 B = 72 pieces of 16 B): piece p of row m is stored at
+// piece position p ^ mla_swz(m), a permutation inside each aligned group of 8
+// pieces.  Rows copied to LDS unchanged then let 8 consecutive rows read the
+// same piece, and 4 consecutive rows read two adjacent pieces, without bank
+// conflicts.
+HXHD int mla_swz(int m) { return 2 * (m & 3) + ((m >> 2) & 1); }
 
 // Element (row m, column d) -> 2 * byte offset + nibble (nibble is 1 for the
 // high half of an FP4 byte).  `width` is the row width for row layouts.
@@ -77,8 +84,10 @@ HXHD int64_t tile_off2(int lay, int width, int m, int d) {
       const int ni = nb * 4 + j;
       return 2 * (int64_t)((hq * 16 + c) * 16 + (ni >> 1)) + (ni & 1);
     }
-    case kLayRowBf16:
-      return 2 * ((int64_t)m * width + d) * 2;
+    case kLayMlaBf16: {
+      const int p = (d >> 3) ^ mla_swz(m);
+      return 2 * ((int64_t)m * width * 2 + p * 16 + (d & 7) * 2);
+    }
     case kLayRowU8:
     default:
       return 2 * ((int64_t)m * width + d);
@@ -128,10 +137,13 @@ HXHD void tile_inv(int lay, int width, int64_t off2, int* m, int* d) {
       *d = (ni >> 2) * 16 + (lane & 15);
       return;
     }
-    case kLayRowBf16:
-      *m = (b >> 1) / width;
-      *d = (b >> 1) % width;
+    case kLayMlaBf16: {
+      const int row = b / (width * 2);
+      const int p = ((b % (width * 2)) >> 4) ^ mla_swz(row);
+      *m = row;
+      *d = p * 8 + ((b & 15) >> 1);
       return;
+    }
     case kLayRowU8:
     default:
       *m = b / width;

@@ -199,6 +199,9 @@ PARITY_CASES = [
     configs.MXFP4_RAGGED.scaled(B=3, ctx_range=(1, 30000)),
     configs.LLAMA405B_SHARE.scaled(B=2, Hq=2, ctx=None, ctx_range=(100, 9000), P=5),      # G=2
     configs.TINY_GQA.scaled(B=1, Hq=1, ctx=3333, P=1),                                     # P=1, G=1
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4),                 # MLA, ragged
+    configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(1, 40), P=8),                   # MLA, empty slices
+    configs.DEEPSEEK_MLA.scaled(B=1, ctx=20011, P=2),                                     # MLA, many splits
 ]
 
 
