@@ -3,28 +3,28 @@
 // per latent head (the DeepSeek-R1 shape of the Helix review, Prompt 1.4.1;
 // the Helix summary notes MLA effectively has one KV head).
 //
-// The query-group contraction is dense here (128 heads share every latent
-// row), so both products run on v_mfma_f32_32x32x16_bf16:
+// Both products are dense (128 heads share every latent row) and run on
+// v_mfma_f32_32x32x16_bf16:
 //   S^T[32 tokens][32 heads] = K[32 tokens][576] . Q^T[576][32 heads]
 //   O^T[512][32 heads]      += V^T[512][32 tokens] . P^T[32 tokens][32 heads]
 //
-// A workgroup of eight waves streams a run of 32-token tiles of one slice.
-// Wave w works on head group hg = w % 4 (heads 32 hg .. +31) and half
-// dh = w / 4 of both contractions: k-steps 18 dh .. +17 of the score product
-// (its Q^T fragments: 12 in VGPRs, 6 parked in LDS) and value blocks
-// 8 dh .. +7 of the output (its accumulator, 128 VGPRs).  The two waves of a
-// head group add their partial scores through LDS, so both hold the same
-// scores and run the same softmax.  With everything in VGPRs the softmax
-// rescale is a plain multiply and two waves fit on each SIMD.
+// A workgroup of four waves (one per SIMD, 512 registers each) streams a run
+// of 32-token tiles of one slice.  Wave w owns heads 32 w .. 32 w + 31: their
+// Q^T fragments for all 576 columns stay in VGPRs (144 registers), their
+// O^T accumulator for all 512 value columns in AGPRs (256 registers), so a
+// wave needs nothing from the other waves but the shared tile: no partial
+// sums are exchanged and every score is computed once.  The softmax keeps
+// the first tile's max as its reference, so the accumulator never needs
+// rescaling (a score more than 2^kHeadroom above it restarts the run).
 //
 // A tile (two chunk tiles, 36 KiB) is copied from HBM into LDS unchanged with
-// direct global-to-LDS loads (no VGPRs), the next tile loading while one is
-// used.  The cache
-// stores each latent row with its 16-byte pieces XOR-swizzled inside aligned
-// groups of 8, so the unchanged copy is already bank-conflict free for both
-// views: every wave reads the K view with 16-byte LDS loads and the
-// transposed V view with ds_read_b64_tr_b16, and one stored copy of the latent
-// row serves both products.
+// direct global-to-LDS loads (no VGPRs), into one of four buffers: three
+// tiles are in flight while one is used, and one barrier per tile both
+// publishes a tile and frees the buffer for the copy three tiles ahead.  The
+// cache stores each latent row with its 16-byte pieces XOR-swizzled inside
+// aligned groups of 8, so the unchanged copy is read efficiently both as
+// 16-byte rows (score operand) and through ds_read_b64_tr_b16 (transposed
+// value operand), and one stored copy of the latent row serves both.
 //
 // Lane layouts used below (64-lane wave, l = lane, half = l / 32):
 //   32x32x16 A operand: row l % 32, k = 8 * half + j (j = 0..7);
@@ -33,53 +33,47 @@
 //   ds_read_b64_tr_b16, per group of 16 lanes: lane i receives element i % 4
 //   of the 4-element reads of lanes i / 4 + 4 k, k = 0..3.
 
+#include <type_traits>
+
 #include "hx_common.h"
 
 namespace hx {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeadsPerGroup = 32;
+constexpr int kHeadsPerWave = 32;
 constexpr int kDk = 576;
 constexpr int kDv = 512;
 constexpr int kTileTok = 32;                       // tokens per LDS tile (two chunk tiles)
 constexpr int kRowBytes = kDk * 2;                 // 1152
 constexpr int kTileBytes = kTileTok * kRowBytes;   // 36 KiB
-constexpr int kTileBlocks = kTileBytes / 1024;     // 1 KiB direct loads per tile (36)
-constexpr int kNBuf = 2;                           // tiles in flight
+constexpr int kBlocksPerWave = kTileBytes / 1024 / kWaves;   // 1 KiB copies per wave per tile (9)
+constexpr int kNBuf = 4;                           // tile buffers
 constexpr int kSteps = kDk / 16;                   // k-steps of the score product (36)
-constexpr int kHalfSteps = kSteps / 2;             // per wave (18)
 constexpr int kVBlocks = kDv / 32;                 // 32-column value blocks (16)
-constexpr int kHalfVBlocks = kVBlocks / 2;         // per wave (8)
-constexpr int kQLds = 6;                           // of a wave's 18 Q^T fragments, the first 6 live in LDS
+constexpr int kKPre = 4;                           // score operands read ahead
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kHeadroom = 64.0f;                 // log2 of the largest unnormalised P
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint4 lds_u4;
-typedef __attribute__((address_space(3))) f32x4 lds_f4;
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // One direct global-to-LDS load of 16 bytes per lane: lane l's bytes from
 // sbase + voff land at LDS byte lds + 16 l (M0 holds the wave-uniform LDS
 // base).  Issued from inline assembly so the compiler does not treat the
 // address registers as pending load results (it would otherwise wait for the
-// next tile's loads before every reuse of those registers).  Completion is
-// awaited with explicit vmcnt waits before the barrier that publishes a tile;
-// no other M0 user is live in the kernel.
+// tile loads before every reuse of those registers).  Completion is awaited
+// with explicit vmcnt waits before the barrier that publishes a tile; no
+// other M0 user is live in the kernel.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
   const uint64_t sb = (uint64_t)sbase;
   const uint64_t sbu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
@@ -89,33 +83,53 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
                : "memory");
 }
 
-// Workgroup barrier after this wave's outstanding loads have landed: global
-// (and direct-to-LDS) loads down to VMCNT still in flight, all LDS accesses
-// done.  The asm is also a compiler memory barrier, so no LDS access moves
-// across it.
+// Workgroup barrier after this wave's loads down to VMCNT still in flight
+// have landed and all its LDS accesses are done.  The asm is also a compiler
+// memory barrier, so no LDS access moves across it.
 template <int VMCNT>
 __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VMCNT) : "memory");
+}
+
+// Score-product step with the accumulator in VGPRs (the AGPRs hold the value
+// accumulator).  Back-to-back steps on the same accumulator need no wait
+// states; the first VALU read of the result needs more than 18, which the
+// caller provides.
+__device__ __forceinline__ f32x16 mfma_s(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ f32x16 mfma_s0(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+
+// The lane index, opaque to the optimiser: addresses derived from it inside
+// the tile loop are recomputed there (a few integer ops) instead of being
+// hoisted out and kept live in VGPRs across the loop.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-__global__ __launch_bounds__(kThreads) void mla_partial_kernel(const PartialArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNBuf][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) float s_part[kWaves][16][64];   // partial scores per wave
-  // Q^T fragments that do not fit in registers next to the accumulator:
-  // [wave][step][lane] x 16 B; each lane reads back only what it wrote.
-  __shared__ __attribute__((aligned(1024))) uint8_t s_q[kWaves][kQLds][1024];
+  // 1 when a wave saw a score beyond its headroom; two sets, by the parity of
+  // the iteration, so that a wave writing the next flag cannot overtake a
+  // slower wave still reading the current ones
+  __shared__ uint32_t s_over[2][kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int hg = wave & 3;     // head group
-  const int dh = wave >> 2;    // contraction half
 
   // ---- which (request, latent head, slice, split) this workgroup owns
   const int wg = blockIdx.x;
@@ -138,179 +152,203 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(const PartialArgs
   const int64_t tile0 = ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
   const uint8_t* base = a.k + tile0 * a.k_tile + t_begin * kRowBytes;   // latent rows, 1152 B each
 
-  // ---- Q^T fragments of head 32 hg + col for k-steps 18 dh .. +17 (B
-  //      operand: step s covers columns 16 s + 8 half .. +7)
-  bf16x8 qf[kHalfSteps - kQLds];
+  // ---- Q^T fragments of head 32 wave + col (B operand: step s covers
+  //      columns 16 s + 8 half .. +7)
+  bf16x8 qf[kSteps];
   {
-    const int head = g * a.G + kHeadsPerGroup * hg + col;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + head) * kDk + 16 * kHalfSteps * dh + 8 * half;
+    const int head = g * a.G + kHeadsPerWave * wave + col;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + head) * kDk + 8 * half;
 #pragma unroll
-    for (int s = 0; s < kQLds; ++s)
-      *(lds_u4*)((lds_u8*)&s_q[wave][s][0] + 16 * lane) = *reinterpret_cast<const uint4*>(qrow + 16 * s);
-#pragma unroll
-    for (int s = kQLds; s < kHalfSteps; ++s)
-      qf[s - kQLds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+    for (int s = 0; s < kSteps; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
   }
-  const lds_u8* q_lds = (const lds_u8*)&s_q[wave][0][0] + 16 * lane;
   // Q is in place before any tile load is issued, so no wait the compiler
   // derives for Q can later count the tile loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- direct global -> LDS copy of tile k into buffer buf: 1 KiB blocks
-  //      w, w + 8, ... (waves 0-3 move five, 4-7 four); lane l moves bytes
-  //      16 l .. +15 of each.  Rows past the slice end (last tile only) are
-  //      fetched from row 0 of the tile instead: finite values that the
-  //      masked scores give weight 0.
-  const int nload = wave < 4 ? 5 : 4;
-  const uint32_t lane_off = 16u * lane;
-  auto load_tile = [&](int k, int buf) {
+  // ---- direct global -> LDS copy of tile k into buffer k % 4: 1 KiB blocks
+  //      w, w + 4, ..., w + 32; lane l moves bytes 16 l .. +15 of each.  Rows
+  //      past the slice end (last tile only) are fetched from row 0 of the
+  //      tile instead: finite values that the masked scores give weight 0.
+  auto load_tile = [&](int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
     const uint8_t* src = base + (int64_t)k * kTileBytes;
-    uint8_t* dst = &s_tile[buf][0];
+    uint8_t* dst = &s_tile[k % kNBuf][0];
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
+    for (int j = 0; j < kBlocksPerWave; ++j) {
       const int blk = wave + kWaves * j;
-      uint32_t off = blk * 1024u + lane_off;   // byte of the tile this lane moves
+      uint32_t off = blk * 1024u + 16u * opaque_lane();   // byte of the tile this lane moves
       if (valid < kTileTok && off / kRowBytes >= (uint32_t)valid) off %= kRowBytes;
-      if (j < 4 || wave < 4) dma16(off, src, lds_addr(dst + blk * 1024));
+      dma16(off, src, lds_addr(dst + blk * 1024));
     }
   };
 
-  f32x16 acc[kHalfVBlocks];
+  f32x16 acc[kVBlocks];
 #pragma unroll
-  for (int i = 0; i < kHalfVBlocks; ++i) acc[i] = f32x16{};
-  float mrun = -INFINITY;   // running max of head 32 hg + col (base 2)
-  float lsum = 0.f, lsum_mfma = 0.f;
+  for (int i = 0; i < kVBlocks; ++i) acc[i] = f32x16{};
+  float mref = -INFINITY;   // reference max of head 32 wave + col (base 2)
+  float lsum = 0.f;         // sum of P over this lane's tokens (exact)
+  float lsum_mfma = 0.f;    // the same over the bf16-rounded P
   const float c2 = a.c2;
 
-  // per-lane LDS byte offsets inside a tile.  K view: row col, piece
-  // 2 s + half + 36 dh, swizzled by row; 4 consecutive k-steps move 8 pieces
-  // (128 B), so offsets repeat with period 4 plus an immediate.
-  const int swk = mla_swz(col);
-  int k_off[4];   // steps s and s + 4 differ by 8 pieces (128 B): four bases, immediate offsets
+  // Score view: row col, piece 2 s + half, swizzled by the row; steps s and
+  // s + 4 differ by 8 pieces (128 B): four bases plus immediate offsets.
+  int k_off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int pc = 2 * s + half + 2 * kHalfSteps * dh;
-    k_off[s] = kRowBytes * col + 16 * ((pc & ~7) | ((pc & 7) ^ swk));
+    const int pc = 2 * s + half;
+    k_off[s] = kRowBytes * col + 16 * ((pc & ~7) | ((pc & 7) ^ mla_swz(col)));
   }
-  // V view for ds_read_b64_tr_b16: lane i16 of its 16-lane group reads row
-  // 16 u + 4 half + i16 / 4 (+ 8 for the second half of the k-step), columns
-  // 32 nb + 16 cb + 4 (i16 % 4) .. +3, i.e. piece 4 nb + 2 cb + (i16 % 4) / 2;
-  // value blocks 8 dh + nb.  nb and nb + 2 differ by 8 pieces: two bases.
+  // Value view for ds_read_b64_tr_b16: lane i16 of its 16-lane group reads
+  // row 16 u + 4 half + i16 / 4 (+ 8 for the second half of the k-step),
+  // columns 32 nb + 16 cb + 4 (i16 % 4) .. +3, i.e. piece
+  // 4 nb + 2 cb + (i16 % 4) / 2.  nb and nb + 2 differ by 8 pieces; rows r
+  // and r + 16 share the swizzle: two bases for each of the two row halves.
   const int i16 = lane & 15;
   const int cb = (lane >> 4) & 1;
-  const int vrow = 4 * half + (i16 >> 2);
-  const int swv = mla_swz(vrow);   // rows + 8 and + 16 share the swizzle
-  int v_off[2];
+  int v_off[2][2];   // [row half][nb & 1]
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int pc = 4 * (kHalfVBlocks * dh + e) + 2 * cb + ((i16 & 3) >> 1);
-    v_off[e] = kRowBytes * vrow + 16 * ((pc & ~7) | ((pc & 7) ^ swv)) + 8 * (i16 & 1);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int vrow = 4 * half + (i16 >> 2) + 8 * hh;
+    const int swv = mla_swz(vrow);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int pc = 4 * e + 2 * cb + ((i16 & 3) >> 1);
+      v_off[hh][e] = kRowBytes * vrow + 16 * ((pc & ~7) | ((pc & 7) ^ swv)) + 8 * (i16 & 1);
+    }
   }
-  lds_f4* my_part = (lds_f4*)&s_part[wave][0][0] + lane;
-  const lds_f4* other_part = (const lds_f4*)&s_part[wave ^ 4][0][0] + lane;
 
-  // tile k + 1 loads while tile k is used
-  if (ntiles > 0) load_tile(0, 0);
-  for (int k = 0; k < ntiles; ++k) {
-    const int buf = k % kNBuf;
-    if (k + 1 < ntiles) {
-      load_tile(k + 1, (k + 1) % kNBuf);
-      // wait for tile k's blocks: the newer loads are tile k + 1's
-      if (wave < 4) wait_barrier<5>();
-      else wait_barrier<4>();
-    } else {
-      wait_barrier<0>();
-    }
-    const lds_u8* tb = (const lds_u8*)&s_tile[buf][0];
+  // ---- the two products of a tile, as steps that can be interleaved
+  auto kread = [&](const lds_u8* tb, int s) { return *(const lds_u4*)(tb + k_off[s & 3] + 128 * (s >> 2)); };
+  auto vread = [&](const lds_u8* tb, int i) {   // i = 16 u + nb
+    const int nb = i & 15;
+    const int rel = 128 * (nb >> 1) + kRowBytes * 16 * (i >> 4);
+    const uint2 lo =
+        __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + v_off[0][nb & 1] + rel)));
+    const uint2 hi =
+        __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + v_off[1][nb & 1] + rel)));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
 
-    // ---- partial scores over this wave's 18 k-steps
-    f32x16 sc = {};
-    uint4 kv[kHalfSteps];
-    uint4 qv[kQLds];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) kv[s] = *(const lds_u4*)(tb + k_off[s & 3] + 128 * (s >> 2));
-#pragma unroll
-    for (int s = 0; s < 2; ++s) qv[s] = *(const lds_u4*)(q_lds + 1024 * s);
-#pragma unroll
-    for (int s = 0; s < kHalfSteps; ++s) {
-      if (s + 2 < kHalfSteps) kv[s + 2] = *(const lds_u4*)(tb + k_off[(s + 2) & 3] + 128 * ((s + 2) >> 2));
-      if (s + 2 < kQLds) qv[s + 2] = *(const lds_u4*)(q_lds + 1024 * (s + 2));
-      const bf16x8 qb = s < kQLds ? __builtin_bit_cast(bf16x8, qv[s < kQLds ? s : 0]) : qf[s < kQLds ? 0 : s - kQLds];
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv[s]), qb, sc, 0, 0, 0);
-    }
-    // ---- add the other half's partial scores (same lanes, same registers)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) my_part[64 * i] = f32x4{sc[4 * i], sc[4 * i + 1], sc[4 * i + 2], sc[4 * i + 3]};
-    wait_barrier<63>();   // the partial scores are in LDS (tile loads may still fly)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 o = other_part[64 * i];
-      // fixed order (half 0's partial first) so both waves of the pair get identical sums
-      if (dh == 0) {
-        sc[4 * i] += o.x; sc[4 * i + 1] += o.y; sc[4 * i + 2] += o.z; sc[4 * i + 3] += o.w;
-      } else {
-        sc[4 * i] = o.x + sc[4 * i]; sc[4 * i + 1] = o.y + sc[4 * i + 1];
-        sc[4 * i + 2] = o.z + sc[4 * i + 2]; sc[4 * i + 3] = o.w + sc[4 * i + 3];
-      }
-    }
+  // ---- online softmax (base 2) of one tile's scores against a fixed
+  //      reference max per head: the first tile's max.  P = 2^(s - mref) is
+  //      then not bounded by 1 but by 2^kHeadroom as long as no later score
+  //      exceeds the reference by more than kHeadroom; bf16 P and the fp32
+  //      sums hold such values exactly as well as values below 1.  A score
+  //      beyond that (seen by any wave) restarts the run with the larger
+  //      reference, so the accumulator never needs rescaling.  The result is
+  //      unchanged: O and the sums share the reference, and
+  //      LSE = mref + log2(sum).  P goes out as bf16 pairs in pk.
+  uint32_t pk[8];
+  float mseen = -INFINITY;   // largest scaled score seen in this run (base 2)
+  auto softmax = [&](f32x16 sc, int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
     if (valid < kTileTok) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + 4 * half + (i & 3) >= valid) sc[i] = -INFINITY;
     }
-
-    // ---- online softmax (base 2)
     float cm = sc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) cm = fmaxf(cm, sc[i]);
     cm = fmaxf(cm, __shfl_xor(cm, 32)) * c2;
-    const float mnew = fmaxf(mrun, cm);
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-#pragma unroll
-    for (int i = 0; i < kHalfVBlocks; ++i) acc[i] *= alpha;
-    lsum *= alpha;
-    lsum_mfma *= alpha;
-    mrun = mnew;
-    uint32_t pk[8];
+    mseen = fmaxf(mseen, cm);
+    if (mref == -INFINITY) mref = cm;   // first tile of the run (at least one valid token)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i], c2, -mrun));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i + 1], c2, -mrun));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i], c2, -mref));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i + 1], c2, -mref));
       lsum += p0 + p1;
-      pk[i] = pack_bf16(p0, p1);
-      lsum_mfma += bf16lo(pk[i]) + bf16hi(pk[i]);
+      const bf16x2 pb2 = {(__bf16)p0, (__bf16)p1};
+      pk[i] = __builtin_bit_cast(uint32_t, pb2);
+      // the rounded values the matrix product uses, summed for the normalisation
+      lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, lsum_mfma, false);
     }
+  };
 
-    // ---- O^T += V^T P^T over this wave's 8 value blocks.  k-step u takes P
-    //      registers 8u..8u+7 = tokens 16u + 4 half + (0..3) and
-    //      16u + 8 + 4 half + (0..3); the V^T operand is two transposed reads.
-    auto vread = [&](int i) {   // i = 8u + nb
-      const int nb = i & 7;
-      const lds_u8* vp = tb + v_off[nb & 1] + 128 * (nb >> 1) + kRowBytes * 16 * (i >> 3);
-      const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp));
-      const uint2 hi =
-          __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + kRowBytes * 8)));
-      return make_uint4(lo.x, lo.y, hi.x, hi.y);
-    };
-    uint4 vv[2 * kHalfVBlocks];
-    vv[0] = vread(0);
+  // ---- tiles, software-pipelined: iteration k accumulates tile k's values
+  //      (O^T += V^T P^T, 32 products into 16 independent accumulators)
+  //      interleaved with tile k + 1's scores (S^T = K Q^T, a chain of 36),
+  //      then runs tile k + 1's softmax; iteration -1 only scores tile 0.
+  //      Tiles 0-2 are copied up front and tile k + 3 into the buffer of
+  //      tile k - 1 once every wave is past it (the barrier).  Loads
+  //      complete in issue order, so tile k + 1 has landed once only tile
+  //      k + 2's copy may still be pending.  Each barrier also publishes
+  //      every wave's overflow flag for the tile scored before it.
+  // One iteration: wait for tile k + 1 and publish the overflow flags, then
+  // the interleaved products.  CUR: tile k's values exist (k >= 0); NEXT:
+  // tile k + 1 exists.  Returns true when some wave asks for a restart.
+  auto iteration = [&](auto cur_t, auto next_t, int k) -> bool {
+    constexpr bool CUR = decltype(cur_t)::value;
+    constexpr bool NEXT = decltype(next_t)::value;
+    const int par = k & 1;
+    const bool over = __any(mseen > mref + kHeadroom);   // all lanes vote, outside the lane-0 branch
+    if (lane == 0) s_over[par][wave] = over ? 1u : 0u;
+    if (k + 2 < ntiles) wait_barrier<kBlocksPerWave>();
+    else wait_barrier<0>();
+    if ((s_over[par][0] | s_over[par][1] | s_over[par][2] | s_over[par][3]) != 0) return true;
+    if (CUR && k + 3 < ntiles) load_tile(k + 3);
+    const lds_u8* tv = (const lds_u8*)&s_tile[(k + kNBuf) % kNBuf][0];
+    const lds_u8* tk = (const lds_u8*)&s_tile[(k + 1) % kNBuf][0];
+    f32x16 sc;
+    uint4 kv[kKPre + 1];
+    uint4 vv[3];
+    if (NEXT) {
 #pragma unroll
-    for (int i = 0; i < 2 * kHalfVBlocks; ++i) {
-      if (i + 1 < 2 * kHalfVBlocks) vv[i + 1] = vread(i + 1);
-      const int u = i >> 3, nb = i & 7;
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[i]), pb, acc[nb], 0, 0, 0);
+      for (int s = 0; s < kKPre; ++s) kv[s] = kread(tk, s);
     }
-    wait_barrier<63>();   // every wave is done with this buffer and the partial scores
+    if (CUR) {
+      vv[0] = vread(tv, 0);
+      vv[1] = vread(tv, 1);
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (CUR && s < 2 * kVBlocks) {
+        if (s + 2 < 2 * kVBlocks) vv[(s + 2) % 3] = vread(tv, s + 2);
+        const int u = s >> 4;
+        const bf16x8 pb =
+            __builtin_bit_cast(bf16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
+        acc[s & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[s % 3]), pb, acc[s & 15],
+                                                              0, 0, 0);
+      }
+      if (NEXT) {
+        if (s + kKPre < kSteps) kv[(s + kKPre) % (kKPre + 1)] = kread(tk, s + kKPre);
+        sc = s == 0 ? mfma_s0(__builtin_bit_cast(bf16x8, kv[0]), qf[0])
+                    : mfma_s(__builtin_bit_cast(bf16x8, kv[s % (kKPre + 1)]), qf[s], sc);
+      }
+    }
+    if (NEXT) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");   // the last score step has drained
+      softmax(sc, k + 1);
+    }
+    return false;
+  };
+  typedef std::integral_constant<bool, true> T;
+  typedef std::integral_constant<bool, false> F;
+
+  for (;;) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < ntiles) load_tile(j);
+    bool restart = ntiles > 0 && iteration(F{}, T{}, -1);
+    for (int k = 0; !restart && k + 1 < ntiles; ++k) restart = iteration(T{}, T{}, k);
+    if (!restart && ntiles > 0) restart = iteration(T{}, F{}, ntiles - 1);
+    if (!restart) break;
+    // a score outgrew the reference: every wave starts over from the first
+    // tile with its largest score so far as the reference (rare: needs a
+    // jump of 2^kHeadroom over the run's first tile)
+    wait_barrier<0>();   // no copy is still writing a buffer; every wave has read the flags
+#pragma unroll
+    for (int i = 0; i < kVBlocks; ++i) acc[i] = f32x16{};
+    lsum = 0.f;
+    lsum_mfma = 0.f;
+    mref = mseen;
   }
 
-  // ---- finalize: this wave's heads, its half of the value columns
+  // ---- finalize: head 32 wave + col, all 512 value columns
   lsum += __shfl_xor(lsum, 32);
   lsum_mfma += __shfl_xor(lsum_mfma, 32);
   const int G = a.G;
-  const int hd = kHeadsPerGroup * hg + col;   // head inside the group
+  const int hd = kHeadsPerWave * wave + col;   // head inside the group
   float* out_o;
   float* out_l;
   if (nsplit == 1) {
@@ -322,15 +360,15 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(const PartialArgs
   }
   const float inv = lsum_mfma > 0.f ? 1.0f / lsum_mfma : 0.f;
 #pragma unroll
-  for (int nb = 0; nb < kHalfVBlocks; ++nb) {
+  for (int nb = 0; nb < kVBlocks; ++nb) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 v = make_float4(acc[nb][4 * q4] * inv, acc[nb][4 * q4 + 1] * inv, acc[nb][4 * q4 + 2] * inv,
                                    acc[nb][4 * q4 + 3] * inv);
-      *reinterpret_cast<float4*>(out_o + 32 * (kHalfVBlocks * dh + nb) + 8 * q4 + 4 * half) = v;
+      *reinterpret_cast<float4*>(out_o + 32 * nb + 8 * q4 + 4 * half) = v;
     }
   }
-  if (half == 0 && dh == 0) *out_l = lsum > 0.f ? (mrun + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (half == 0) *out_l = lsum > 0.f ? (mref + __log2f(lsum)) * kLn2 : -INFINITY;
 #endif
 }
 

@@ -224,6 +224,45 @@ def test_decode_step_matches_oracle(w, needles):
     H.log(f"   ctx={inp.ctx} worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
 
 
+def _slice_row_to_token(j, r, P):
+    """Token index of local row j of slice r (the inverse of the placement)."""
+    return ((j // 16) * P + r) * 16 + j % 16
+
+
+@pytest.mark.parametrize("staircase", [False, True], ids=["one-jump", "staircase"])
+def test_mla_large_score_jumps(staircase):
+    """Scores far above everything seen earlier in a run of tiles (more than
+    2^64 in base 2): the MLA kernel keeps the first tile's max as its softmax
+    reference and must start the run over with a larger one.  Rows aligned
+    with one head's query get natural-log scores of 50-160, placed past the
+    first tiles of runs in both slices, for heads served by different waves;
+    the staircase raises one head's score three times within one run."""
+    w = configs.DEEPSEEK_MLA.scaled(B=1, ctx=200000, P=2)
+    inp = synth.make_inputs(w, 17, device=DEV)
+    k = inp.k[0, 0]                             # [n, 576] bf16
+
+    def plant(j, r, h, target):
+        t = _slice_row_to_token(j, r, w.P)
+        qh = inp.q[0, h].float()
+        alpha = target / (w.softmax_scale * float(qh.norm()))
+        k[t] = (alpha * qh / qh.norm()).to(torch.bfloat16)
+
+    if staircase:
+        for r, h in ((0, 0), (1, 77)):
+            for j, target in ((100, 50.0), (300, 100.0), (700, 160.0)):
+                plant(j, r, h, target)
+    else:
+        for i, (j, r) in enumerate(((40, 0), (100, 1), (1530, 0), (2210, 1), (3000, 0), (60000, 1))):
+            plant(j, r, (0, 45, 77, 127, 33, 100)[i], 60.0)
+    H.log(f"[jumps] staircase={staircase}")
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label=f"jumps staircase={staircase}")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
 def test_partials_are_deterministic_and_workspace_reusable():
     w = configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(5000, 60000))
     inp = synth.make_inputs(w, 4, device=DEV)
