@@ -55,19 +55,19 @@ def setup(w, seed):
     return inp, cache, step_in, ws, o_part, lse_part, o, lse
 
 
-def kernel_src_hash():
-    """Hash of the GQA kernel sources, to tell whether recorded counters
-    still describe the kernel that runs."""
+def kernel_src_hash(w):
+    """Hash of the partial kernel's sources for workload w, to tell whether
+    recorded counters still describe the kernel that runs."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for p in ("decode_gqa.hip", "hx_common.h"):
+    for p in ("decode_mla.hip" if w.v_alias_k else "decode_gqa.hip", "hx_common.h"):
         with open(os.path.join(here, "long_context_decode_split_amd", "csrc", p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload):
+def recorded_traffic(w):
     """HBM bytes per launch of the partial kernel from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json (scaled by
     a copy of known size), or None when none was recorded for this workload
@@ -75,10 +75,10 @@ def recorded_traffic(workload):
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f).get(w.name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_src_sha16") != kernel_src_hash():
+    if not rec or rec.get("kernel_src_sha16") != kernel_src_hash(w):
         return None
     return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
@@ -233,7 +233,7 @@ def main():
             "peak": peak_gbs,
             "unit": "GB/s",
             "frac": round(kern_gbs / peak_gbs, 4),
-            "traffic": recorded_traffic(w.name),
+            "traffic": recorded_traffic(w),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
         },
