@@ -62,39 +62,42 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
 
   const int64_t byte0 = piece * 16;
   const int nbytes = (int)((a.tile_bytes[plane] - byte0) < 16 ? (a.tile_bytes[plane] - byte0) : 16);
-  const bool whole = row0 >= pos && row0 + kChunk <= end;
-  uint8_t buf[16];
-  if (!whole || nbytes < 16) {
-    for (int i = 0; i < nbytes; ++i) buf[i] = dst[byte0 + i];
-  }
   const int eb = a.ebits[plane];
   const int lay = a.lay[plane], width = a.width[plane];
   const int64_t srow = a.src_row_bytes[plane];
-  if (eb == 16) {
-    for (int e = 0; e < nbytes / 2; ++e) {
-      int mm, d;
-      tile_inv(lay, width, 2 * (byte0 + 2 * e), &mm, &d);
-      const int64_t tok = row0 + mm;
-      if (tok < pos || tok >= end) continue;
-      const uint8_t* s = src + (src_tok0 + (tok - pos)) * srow + 2 * (int64_t)d;
-      buf[2 * e] = s[0];
-      buf[2 * e + 1] = s[1];
-    }
-  } else if (eb == 8) {
-    for (int e = 0; e < nbytes; ++e) {
-      int mm, d;
-      tile_inv(lay, width, 2 * (byte0 + e), &mm, &d);
-      const int64_t tok = row0 + mm;
-      if (tok < pos || tok >= end) continue;
-      buf[e] = src[(src_tok0 + (tok - pos)) * srow + d];
-    }
-  } else {   // 4-bit codes, even element in the low nibble of the source
-    for (int e = 0; e < 2 * nbytes; ++e) {
-      int mm, d;
-      tile_inv(lay, width, 2 * byte0 + e, &mm, &d);
-      const int64_t tok = row0 + mm;
-      if (tok < pos || tok >= end) continue;
-      const uint8_t sb = src[(src_tok0 + (tok - pos)) * srow + (d >> 1)];
+  const int nelem = eb == 16 ? nbytes / 2 : (eb == 8 ? nbytes : 2 * nbytes);
+  auto elem_off2 = [&](int e) -> int64_t {
+    return eb == 16 ? 2 * (byte0 + 2 * e) : (eb == 8 ? 2 * (byte0 + e) : 2 * byte0 + e);
+  };
+  // a piece holding none of the new rows stays as it is
+  bool any = false;
+  for (int e = 0; e < nelem; ++e) {
+    int mm, d;
+    tile_inv(lay, width, elem_off2(e), &mm, &d);
+    any |= row0 + mm >= pos && row0 + mm < end;
+  }
+  if (!any) return;
+  const bool whole = row0 >= pos && row0 + kChunk <= end;
+  uint8_t buf[16];
+  if (nbytes == 16) {
+    const uint4 v = whole ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(dst + byte0);
+    __builtin_memcpy(buf, &v, 16);
+  } else {
+    for (int i = 0; i < nbytes; ++i) buf[i] = dst[byte0 + i];
+  }
+  for (int e = 0; e < nelem; ++e) {
+    int mm, d;
+    tile_inv(lay, width, elem_off2(e), &mm, &d);
+    const int64_t tok = row0 + mm;
+    if (tok < pos || tok >= end) continue;
+    const uint8_t* srcrow = src + (src_tok0 + (tok - pos)) * srow;
+    if (eb == 16) {
+      buf[2 * e] = srcrow[2 * d];
+      buf[2 * e + 1] = srcrow[2 * d + 1];
+    } else if (eb == 8) {
+      buf[e] = srcrow[d];
+    } else {   // 4-bit codes, even element in the low nibble of the source
+      const uint8_t sb = srcrow[d >> 1];
       const uint8_t code = (d & 1) ? (sb >> 4) : (sb & 0xf);
       uint8_t& o = buf[e >> 1];
       o = (e & 1) ? (uint8_t)((o & 0x0f) | (code << 4)) : (uint8_t)((o & 0xf0) | code);
