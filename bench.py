@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="write a 1 GiB buffer before every step (outside the timed events) so that no KV bytes "
+                         "survive in L2 or the 256 MB MALL; steps are then timed one by one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times); used to scale the "
                          "HBM traffic counters of a profiler run")
@@ -180,17 +183,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    new_ev = lambda: torch.cuda.Event(enable_timing=True)
+    kev = [(new_ev(), new_ev()) for _ in range(args.steps)]
+    sev = [(new_ev(), new_ev()) for _ in range(args.steps)]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush_cache else None
+    start, end = new_ev(), new_ev()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        sev[i][0].record(stream)
         step(kev[i])
+        sev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in kev]
+    step_each_ms = [a.elapsed_time(b) for a, b in sev]
     kern_avg_ms = float(np.mean(kern_ms))
+    # back-to-back steps: total over the timed region; flushed steps: each step on its own
+    step_ms = float(np.mean(step_each_ms)) if flush is not None else start.elapsed_time(end) / args.steps
+    pct = lambda x: {f"p{q}": round(float(np.percentile(x, q)) * 1e3, 2) for q in (10, 50, 90)}
 
     nbytes = roofline.kv_bytes(w, inp.ctx)
     flops = roofline.attn_flops(w, inp.ctx)
@@ -238,6 +251,8 @@ def main():
             "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
         },
         "cpu_baseline": cpu,
+        "timing_us": {"step": pct(step_each_ms), "partial": pct(kern_ms),
+                      "cache": "flushed before every step" if flush is not None else "hot (back-to-back steps)"},
     }
     print(json.dumps(out), flush=True)
 
