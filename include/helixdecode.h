@@ -152,6 +152,28 @@ hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const v
                        const void* k_scale_new, const void* v_scale_new, const int64_t* pos, const int32_t* count,
                        int32_t n_new, void* stream);
 
+/* Append new tokens given as bf16 values, quantising them into the cache's
+ * storage format on the device (same placement, pos, count and n_new
+ * conventions as hx_kv_append; the new KV rows of a decode step come out of
+ * the QKV projection and are written round-robin as produced: Helix summary,
+ * paragraph on Helix's two layouts).  k_new [B][Hkv][n_new][Dk] and v_new
+ * [B][Hkv][n_new][Dv] are bf16 (device; v_new NULL if v_alias_k).
+ *   bf16 cache: identical to hx_kv_append.
+ *   fp8 e4m3 cache: per 16-token group of a (request, KV head, K or V),
+ *     scale = amax / 448 (fp32; 1 for an all-zero group) and code = nearest
+ *     e4m3 (ties to even) of x / scale clamped to +-448.  A group filled over
+ *     several calls keeps a scale that only grows: when the new rows' amax
+ *     exceeds 448 * stored scale (and the group holds a non-zero code), the
+ *     scale becomes amax / 448 and the stored codes are re-encoded from
+ *     their values times old / new scale; otherwise new rows use the stored
+ *     scale.  A group written in one call gets exactly the per-group rule.
+ *   MXFP4 cache: per 32 consecutive elements of a row, E = clamp(floor(
+ *     log2 amax) - 2, -127, 127) + 127 and code = nearest e2m1 (ties to
+ *     even, saturating at 6) of x / 2^(E-127); rows are independent.
+ * Deterministic, so equal inputs give equal bytes.  Errors as hx_kv_append. */
+hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                            const int64_t* pos, const int32_t* count, int32_t n_new, void* stream);
+
 /* Decode rows [j0, j0 + n) of slice r, request b, KV head g into fp32:
  * k_out [n][Dk], v_out [n][Dv] (device; v_out may be NULL).  bf16: exact
  * widening; fp8: fp32 product code * scale rounded to nearest-even; MXFP4:

@@ -45,6 +45,7 @@ SIGNATURES = {
     "hx_slice_len": (I32, [I64, I32, I32, P_I64]),
     "hx_kv_tile_offset": (I32, [P_DESC, I32, I32, I32, P_I64]),
     "hx_kv_append": (I32, [P_DESC, P_CACHE, VP, VP, VP, VP, P_I64, P_I32, I32, VP]),
+    "hx_kv_append_bf16": (I32, [P_DESC, P_CACHE, VP, VP, P_I64, P_I32, I32, VP]),
     "hx_kv_dequant": (I32, [P_DESC, P_CACHE, I32, I32, I32, I64, I64, VP, VP, VP]),
     "hx_workspace_size": (I32, [P_DESC, I32, ctypes.POINTER(SZ)]),
     "hx_workspace_init": (I32, [VP, SZ, VP]),

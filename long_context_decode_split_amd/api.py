@@ -126,6 +126,16 @@ def kv_append(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, pos, count
                              _ptr(k_scale_new), _ptr(v_scale_new), _i64(pos), cnt, n_new, _stream(stream)))
 
 
+def kv_append_bf16(cache: KVCache, k_new, v_new, pos, count=None, stream=None):
+    """``hx_kv_append_bf16``: bf16 tensors [B, Hkv, n_new, D] quantised into
+    the cache's storage format on the device; ``pos`` (and ``count``) are
+    host sequences of B ints."""
+    n_new = k_new.shape[2]
+    cnt = None if count is None else (ctypes.c_int32 * len(count))(*[int(c) for c in count])
+    check(lib().hx_kv_append_bf16(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+                                  _i64(pos), cnt, n_new, _stream(stream)))
+
+
 def kv_dequant(cache: KVCache, r, b, g, j0, n, k_out, v_out=None, stream=None):
     check(lib().hx_kv_dequant(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), r, b, g, j0, n, _ptr(k_out),
                               _ptr(v_out), _stream(stream)))

@@ -261,6 +261,68 @@ hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const v
   return HX_OK;
 }
 
+hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                            const int64_t* pos, const int32_t* count, int32_t n_new, void* stream) {
+  g_err[0] = 0;
+  if (!desc || !cache || !pos) return fail(HX_EINVAL, "null argument");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  const hx_kv_desc& d = *desc;
+  if (d.dtype == HX_KV_BF16) return hx_kv_append(desc, cache, k_new, v_new, nullptr, nullptr, pos, count, n_new, stream);
+  if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
+  // quantised caches are GQA caches (Dk = Dv = 128, separate V)
+  if (!cache->k || !k_new || !cache->v || !v_new) return fail(HX_EINVAL, "null K/V plane or input");
+  if (!cache->k_scale || !cache->v_scale) return fail(HX_EINVAL, "null scale plane");
+  const void* ptrs[6] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_new, v_new};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  const int64_t nmax = (int64_t)d.P * d.cap;
+  for (int b = 0; b < d.B; ++b) {
+    const int32_t cnt = count ? count[b] : n_new;
+    if (cnt < 0 || cnt > n_new) return fail(HX_EINVAL, "request %d: count=%d must be in [0, n_new=%d]", b, cnt, n_new);
+    if (pos[b] < 0 || pos[b] + cnt > nmax)
+      return fail(HX_EINVAL, "request %d: pos=%lld, count=%d exceeds P*cap=%lld", b, (long long)pos[b], cnt,
+                  (long long)nmax);
+  }
+  QAppendArgs a{};
+  a.dst[0] = (uint8_t*)cache->k;
+  a.dst[1] = (uint8_t*)cache->v;
+  a.sc[0] = (uint8_t*)cache->k_scale;
+  a.sc[1] = (uint8_t*)cache->v_scale;
+  a.lay[0] = g.lay_k;
+  a.lay[1] = g.lay_v;
+  a.dtype = d.dtype;
+  a.D = d.Dk;
+  a.P = d.P;
+  a.B = d.B;
+  a.Hkv = d.Hkv;
+  a.cap_chunks = d.cap / kChunk;
+  a.tile_bytes = g.k_tile;
+  a.sc_tile_bytes = g.ks_tile;
+  a.n_new = n_new;
+  for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
+    int maxc = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int64_t p0 = pos[b0 + i];
+      const int32_t cnt = count ? count[b0 + i] : n_new;
+      a.pos[i] = p0;
+      a.count[i] = cnt;
+      if (cnt > 0) maxc = std::max(maxc, (int)((p0 + cnt - 1) / kChunk - p0 / kChunk + 1));
+    }
+    if (maxc == 0) continue;
+    a.max_chunks = maxc;
+    a.b0 = b0;
+    const int64_t off = (int64_t)b0 * d.Hkv * n_new * d.Dk;
+    a.src[0] = (const uint16_t*)k_new + off;
+    a.src[1] = (const uint16_t*)v_new + off;
+    s = check_hip(launch_quant_append(a, nb, (hipStream_t)stream), "kv_append_bf16 launch");
+    if (s) return s;
+  }
+  return HX_OK;
+}
+
 hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
                         int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
   g_err[0] = 0;

@@ -195,6 +195,26 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st);
 
+// Quantising append of bf16 rows into fp8 or MXFP4 planes (D = 128).
+struct QAppendArgs {
+  const uint16_t* src[2];  // bf16 rows of K and V, token-major [nb][Hkv][n_new][D] for this launch
+  uint8_t* dst[2];         // code planes
+  uint8_t* sc[2];          // scale planes
+  int lay[2];              // tile layouts
+  int dtype;               // HX_KV_FP8_E4M3 or HX_KV_MXFP4
+  int D;
+  int P, B, Hkv;
+  int64_t cap_chunks;
+  int64_t tile_bytes;      // code bytes per chunk tile
+  int64_t sc_tile_bytes;   // scale bytes per chunk tile
+  int n_new;
+  int max_chunks;
+  int b0;
+  int64_t pos[kMaxBatchPerLaunch];
+  int32_t count[kMaxBatchPerLaunch];
+};
+hipError_t launch_quant_append(const QAppendArgs& a, int nb, hipStream_t st);
+
 struct DequantArgs {
   const uint8_t* k;
   const uint8_t* v;

@@ -214,6 +214,27 @@ def test_append_argument_checks():
     assert call([0, 0], ks=_fake(0x70000)) == _lib.HX_EINVAL   # bf16 takes no scales
 
 
+def test_quantising_append_argument_checks():
+    L = _lib.lib()
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="fp8_e4m3", cap=64)
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, 0x70000, 0x80000)
+
+    def call(pos, count=None, n_new=4, k=0x10000, v=0x20000, c=cache):
+        pa = (ctypes.c_int64 * 2)(*pos)
+        ca = None if count is None else (ctypes.c_int32 * 2)(*count)
+        return L.hx_kv_append_bf16(ctypes.byref(d.c()), ctypes.byref(c), _fake(k), _fake(v), pa, ca, n_new, None)
+
+    assert call([0, 254]) == _lib.HX_EINVAL            # 254 + 4 > P * cap = 256
+    assert call([-1, 0]) == _lib.HX_EINVAL
+    assert call([0, 0], n_new=0) == _lib.HX_EINVAL
+    assert call([0, 0], count=[5, 1]) == _lib.HX_EINVAL   # count > n_new
+    assert call([0, 0], k=0x10002) == _lib.HX_EINVAL      # misaligned
+    assert call([0, 0], v=0) == _lib.HX_EINVAL
+    assert call([0, 0], c=_lib.hx_kv_cache(0x50000, 0x60000, None, 0x80000)) == _lib.HX_EINVAL   # no K scales
+    if not torch.cuda.is_available():
+        assert call([0, 0]) == _lib.HX_EHIP               # valid arguments reach the launch
+
+
 def test_dequant_and_combine_argument_checks():
     L = _lib.lib()
     d = DESCS[0]

@@ -1,0 +1,165 @@
+"""Parity of the quantising append (hx_kv_append_bf16) with the oracle's
+encoders and open-chunk policy (oracle/quantize.py): bit-exact codes and
+scales, read back through hx_kv_dequant, after a prefill and a run of decode
+steps and multi-token appends; then a decode step over the quantised cache
+against the oracle's attention on the oracle's own codes."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_split_amd import api, configs, synth
+from oracle import placement as opl
+from oracle import quantize as oq
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    H.ensure_built()
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def _values(B, Hkv, n, D, seed):
+    """bf16 rows whose magnitude changes from token to token (so fp8 groups
+    raise their scale), with some all-zero rows."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(B, Hkv, n, D, generator=g) * torch.exp2(torch.randint(-3, 1, (B, Hkv, n, 1), generator=g).float())
+    zero = torch.rand(B, Hkv, n, 1, generator=g) < 0.05
+    x = torch.where(zero, torch.zeros_like(x), x)
+    return x.to(torch.bfloat16)
+
+
+def _calls(ctx, seed):
+    """(pos, count) per call: a prefill of part of each request, then decode
+    steps of one token and appends of up to 40 tokens (some requests idle)."""
+    rng = np.random.default_rng(seed)
+    done = [int(rng.integers(0, n // 2 + 1)) for n in ctx]
+    calls = [([0] * len(ctx), list(done))]
+    while any(d < n for d, n in zip(done, ctx)):
+        step = 1 if rng.random() < 0.6 else int(rng.integers(2, 41))
+        cnt = [min(step, n - d) if rng.random() < 0.85 else 0 for d, n in zip(done, ctx)]
+        if sum(cnt) == 0:
+            continue
+        calls.append((list(done), cnt))
+        done = [d + c for d, c in zip(done, cnt)]
+    return calls
+
+
+def _oracle_fp8(x, ctx, calls):
+    """Codes [B, Hkv, n, D] and per-token scales [B, Hkv, n] after the calls."""
+    B, Hkv, n, D = x.shape
+    xf = x.float().numpy()
+    codes = np.zeros((B, Hkv, n, D), dtype=np.uint8)
+    scales = np.ones((B, Hkv, (n + 15) // 16), dtype=np.float32)
+    for pos, cnt in calls:
+        for b in range(B):
+            p0, p1 = pos[b], pos[b] + cnt[b]
+            t = p0
+            while t < p1:
+                c = t // 16
+                row0 = 16 * c
+                hi = min(p1, row0 + 16)
+                for g in range(Hkv):
+                    chunk = np.zeros((16, D), dtype=np.uint8)
+                    m = min(n - row0, 16)
+                    chunk[:m] = codes[b, g, row0:row0 + m]
+                    new, s = oq.append_fp8_chunk(chunk, scales[b, g, c], t - row0, xf[b, g, t:hi])
+                    codes[b, g, row0:row0 + m] = new[:m]
+                    scales[b, g, c] = s
+                t = hi
+    tok_scale = np.repeat(scales, 16, axis=-1)[..., :n]
+    return codes, tok_scale
+
+
+def _oracle_mxfp4(x):
+    B, Hkv, n, D = x.shape
+    packed, E = oq.quantize_mxfp4_rows(x.float().numpy().reshape(-1, D))
+    return packed.reshape(B, Hkv, n, D // 2), E.reshape(B, Hkv, n, D // 32)
+
+
+def _bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+CASES = [
+    configs.FP8_GQA.scaled(B=3, Hkv=2, Hq=8, ctx=None, ctx_range=(1, 400), P=4),
+    configs.MXFP4_RAGGED.scaled(B=3, Hkv=2, Hq=8, ctx_range=(1, 400), P=4),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.dtype)
+def test_quantising_append_matches_oracle(w):
+    ctx = synth.context_lengths(w, 21)
+    nmax = max(ctx)
+    x = _values(w.B, w.Hkv, nmax, w.Dk, seed=22)
+    xv = _values(w.B, w.Hkv, nmax, w.Dv, seed=23)
+    calls = _calls(ctx, seed=24)
+    H.log(f"[quant-append] {w.dtype} ctx={ctx} calls={len(calls)}")
+    cap = synth.capacity(ctx, w.P)
+    desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=False, dtype=w.dtype, cap=cap)
+    cache = api.KVCache(desc, device=DEV, fill=0xFF)
+    kd, vd = x.to(DEV), xv.to(DEV)
+    for pos, cnt in calls:
+        step = max(cnt)
+        kn = torch.stack([torch.nn.functional.pad(kd[b, :, pos[b]:pos[b] + cnt[b]], (0, 0, 0, step - cnt[b]))
+                          for b in range(w.B)]).contiguous()
+        vn = torch.stack([torch.nn.functional.pad(vd[b, :, pos[b]:pos[b] + cnt[b]], (0, 0, 0, step - cnt[b]))
+                          for b in range(w.B)]).contiguous()
+        api.kv_append_bf16(cache, kn, vn, pos=pos, count=cnt)
+    torch.cuda.synchronize()
+
+    if w.dtype == "fp8_e4m3":
+        kc, ks = _oracle_fp8(x, ctx, calls)
+        vc, vs = _oracle_fp8(xv, ctx, calls)
+        inp = synth.Inputs(w=w, seed=0, ctx=ctx, cap=cap, q=None, k=torch.from_numpy(kc), v=torch.from_numpy(vc),
+                           k_scale=torch.from_numpy(ks), v_scale=torch.from_numpy(vs))
+    else:
+        kc, ke = _oracle_mxfp4(x)
+        vc, ve = _oracle_mxfp4(xv)
+        inp = synth.Inputs(w=w, seed=0, ctx=ctx, cap=cap, q=None, k=torch.from_numpy(kc), v=torch.from_numpy(vc),
+                           k_scale=torch.from_numpy(ke), v_scale=torch.from_numpy(ve))
+    # stored bytes, read back through the library's bit-exact decoder
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            K, V = H.token_values(inp, b, g)
+            for r in range(w.P):
+                toks = opl.slice_tokens(ctx[b], w.P, r)
+                if not toks:
+                    continue
+                ko = torch.empty(len(toks), w.Dk, dtype=torch.float32, device=DEV)
+                vo = torch.empty(len(toks), w.Dv, dtype=torch.float32, device=DEV)
+                api.kv_dequant(cache, r, b, g, 0, len(toks), ko, vo)
+                kr = K[toks].astype(np.float32)
+                vr = V[toks].astype(np.float32)
+                assert np.array_equal(_bits(ko.cpu().numpy()), _bits(kr)), f"K rows of b={b} g={g} slice={r}"
+                assert np.array_equal(_bits(vo.cpu().numpy()), _bits(vr)), f"V rows of b={b} g={g} slice={r}"
+
+    # a decode step over the quantised cache against the oracle on its own codes
+    gq = torch.Generator(device=DEV).manual_seed(25)
+    inp.q = (torch.randn(w.B, w.Hq, w.Dk, generator=gq, device=DEV)).to(torch.bfloat16)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label=f"quantised {w.dtype}")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
+def test_bf16_cache_append_is_plain_placement():
+    w = configs.TINY_GQA.scaled(B=2, Hkv=2, Hq=4, ctx=None, ctx_range=(1, 200), P=3)
+    ctx = synth.context_lengths(w, 5)
+    x = _values(w.B, w.Hkv, max(ctx), w.Dk, seed=6).to(DEV)
+    xv = _values(w.B, w.Hkv, max(ctx), w.Dv, seed=7).to(DEV)
+    cap = synth.capacity(ctx, w.P)
+    desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=False, dtype="bf16", cap=cap)
+    a = api.KVCache(desc, device=DEV, fill=0xFF)
+    b = api.KVCache(desc, device=DEV, fill=0xFF)
+    api.kv_append_bf16(a, x, xv, pos=[0] * w.B, count=ctx)
+    api.kv_append(b, x, xv, None, None, pos=[0] * w.B, count=ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
