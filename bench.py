@@ -29,7 +29,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def setup(w, seed):
+def setup(w, seed, append_bf16=False):
     t0 = time.time()
     inp = synth.make_inputs(w, seed, device="cuda")
     desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=w.v_alias_k, dtype=w.dtype, cap=inp.cap)
@@ -44,6 +44,12 @@ def setup(w, seed):
         return torch.stack([t[b, :, last[b]:last[b] + 1] for b in range(w.B)]).contiguous()
 
     step_in = dict(k=newest(inp.k), v=newest(inp.v), ks=newest(inp.k_scale), vs=newest(inp.v_scale), pos=last)
+    if append_bf16:
+        # the newest token as the bf16 values a QKV projection would produce, quantised by the append
+        g = torch.Generator(device="cuda").manual_seed(seed + 1)
+        step_in["kb"] = (torch.randn(w.B, w.Hkv, 1, w.Dk, generator=g, device="cuda") * w.std).to(torch.bfloat16)
+        step_in["vb"] = None if w.v_alias_k else \
+            (torch.randn(w.B, w.Hkv, 1, w.Dv, generator=g, device="cuda") * w.std).to(torch.bfloat16)
     ws = torch.zeros(api.workspace_size(desc, w.Hq), dtype=torch.uint8, device="cuda")
     o_part = torch.empty(w.P, w.B, w.Hq, w.Dv, dtype=torch.float32, device="cuda")
     lse_part = torch.empty(w.P, w.B, w.Hq, dtype=torch.float32, device="cuda")
@@ -141,6 +147,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--append", choices=("codes", "bf16"), default="codes",
+                    help="codes: the step appends the newest token in storage format (hx_kv_append); bf16: as bf16 "
+                         "values quantised on the device (hx_kv_append_bf16)")
     ap.add_argument("--flush-cache", action="store_true",
                     help="write a 1 GiB buffer before every step (outside the timed events) so that no KV bytes "
                          "survive in L2 or the 256 MB MALL; steps are then timed one by one")
@@ -167,11 +176,14 @@ def main():
         sys.exit(2)
 
     w = configs.ALL[args.workload]
-    inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed)
+    inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed, append_bf16=args.append == "bf16")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        api.kv_append(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
+        if args.append == "bf16":
+            api.kv_append_bf16(cache, st["kb"], st["vb"], pos=st["pos"], stream=stream)
+        else:
+            api.kv_append(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
         if ev is not None:
             ev[0].record(stream)
         api.decode_attn_partial(cache, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws, stream=stream)
@@ -238,6 +250,7 @@ def main():
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "Dk": w.Dk, "Dv": w.Dv,
             "v_alias_k": w.v_alias_k, "kv_dtype": w.dtype, "slices": w.P,
             "context": inp.ctx if w.ctx is None else w.ctx, "kv_bytes_per_step": nbytes, "seed": args.seed,
+            "append": "bf16 values quantised on the device" if args.append == "bf16" else "storage format",
         },
         "roofline": {
             "bound": "hbm",

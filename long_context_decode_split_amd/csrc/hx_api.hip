@@ -9,7 +9,7 @@
 #include <cmath>
 #include <mutex>
 
-#include "hx_common.h"
+#include "hx_cache.h"
 
 namespace hx {
 

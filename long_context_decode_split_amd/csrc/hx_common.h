@@ -176,59 +176,6 @@ hx_status fail(hx_status s, const char* fmt, ...);
 hx_status check_hip(hipError_t e, const char* what);
 
 // ---------------------------------------------------------------- launchers
-struct AppendArgs {
-  const uint8_t* src[4];   // k codes, v codes, k scales, v scales (token-major)
-  uint8_t* dst[4];         // planes
-  int lay[4];              // tile layout per plane
-  int width[4];            // row width (row layouts)
-  int ebits[4];            // element bits per plane (16, 8, 4; 32 = fp8 group scale)
-  int64_t src_row_bytes[4];
-  int64_t tile_bytes[4];
-  int nplanes;
-  int P, B, Hkv;
-  int64_t cap_chunks;
-  int n_new;
-  int max_chunks;          // largest number of chunks one request touches
-  int64_t pos[kMaxBatchPerLaunch];
-  int32_t count[kMaxBatchPerLaunch];
-  int b0;                  // first request of this launch
-};
-hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st);
-
-// Quantising append of bf16 rows into fp8 or MXFP4 planes (D = 128).
-struct QAppendArgs {
-  const uint16_t* src[2];  // bf16 rows of K and V, token-major [nb][Hkv][n_new][D] for this launch
-  uint8_t* dst[2];         // code planes
-  uint8_t* sc[2];          // scale planes
-  int lay[2];              // tile layouts
-  int dtype;               // HX_KV_FP8_E4M3 or HX_KV_MXFP4
-  int D;
-  int P, B, Hkv;
-  int64_t cap_chunks;
-  int64_t tile_bytes;      // code bytes per chunk tile
-  int64_t sc_tile_bytes;   // scale bytes per chunk tile
-  int n_new;
-  int max_chunks;
-  int b0;
-  int64_t pos[kMaxBatchPerLaunch];
-  int32_t count[kMaxBatchPerLaunch];
-};
-hipError_t launch_quant_append(const QAppendArgs& a, int nb, hipStream_t st);
-
-struct DequantArgs {
-  const uint8_t* k;
-  const uint8_t* v;
-  const uint8_t* ks;
-  const uint8_t* vs;
-  float* k_out;
-  float* v_out;
-  int dtype, lay_k, lay_v, Dk, Dv, v_alias;
-  int64_t k_tile, v_tile, ks_tile, vs_tile;
-  int64_t plane_tile0;     // tile index of (r, b, g, chunk 0)
-  int64_t j0, n;
-};
-hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
-
 struct PartialArgs {
   const uint8_t* k;
   const uint8_t* v;

@@ -12,7 +12,7 @@
 // stored bytes otherwise.  No two threads touch the same bytes, so the result
 // does not depend on scheduling, and bytes move unconverted (bit-exact).
 
-#include "hx_common.h"
+#include "hx_cache.h"
 
 namespace hx {
 namespace {

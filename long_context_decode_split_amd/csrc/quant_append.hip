@@ -16,7 +16,7 @@
 // MXFP4: per 32 elements of a row, E = clamp(floor(log2 amax) - 2, -127,
 // 127) + 127, code = e2m1 of x / 2^(E-127), saturating at 6.
 
-#include "hx_common.h"
+#include "hx_cache.h"
 
 namespace hx {
 namespace {
