@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--append", choices=("codes", "bf16"), default="codes",
                     help="codes: the step appends the newest token in storage format (hx_kv_append); bf16: as bf16 "
                          "values quantised on the device (hx_kv_append_bf16)")
+    ap.add_argument("--attn", choices=("partial+combine", "one-call"), default="partial+combine",
+                    help="partial+combine: hx_decode_attn_partial then hx_lse_combine (the slice partials are "
+                         "outputs); one-call: hx_decode_attn (final O and LSE only; one launch for small problems)")
     ap.add_argument("--flush-cache", action="store_true",
                     help="write a 1 GiB buffer before every step (outside the timed events) so that no KV bytes "
                          "survive in L2 or the 256 MB MALL; steps are then timed one by one")
@@ -186,6 +189,11 @@ def main():
             api.kv_append(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
         if ev is not None:
             ev[0].record(stream)
+        if args.attn == "one-call":
+            api.decode_attn(cache, inp.q, inp.ctx, w.softmax_scale, o, lse, ws, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         api.decode_attn_partial(cache, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
@@ -251,10 +259,11 @@ def main():
             "v_alias_k": w.v_alias_k, "kv_dtype": w.dtype, "slices": w.P,
             "context": inp.ctx if w.ctx is None else w.ctx, "kv_bytes_per_step": nbytes, "seed": args.seed,
             "append": "bf16 values quantised on the device" if args.append == "bf16" else "storage format",
+            "attention": args.attn,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_attn_partial",
+            "kernel": "decode_attn" if args.attn == "one-call" else "decode_attn_partial",
             "achieved": round(kern_gbs, 2),
             "peak": peak_gbs,
             "unit": "GB/s",

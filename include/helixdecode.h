@@ -181,10 +181,11 @@ hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, co
 hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
                         int64_t j0, int64_t n, float* k_out, float* v_out, void* stream);
 
-/* Workspace bytes hx_decode_attn_partial needs for `desc` with Hq query
- * heads (host only).  The workspace holds the partial results of the splits
- * each slice is cut into; it needs no initialisation and its contents are
- * scratch between calls. */
+/* Workspace bytes hx_decode_attn_partial and hx_decode_attn need for `desc`
+ * with Hq query heads (host only).  The workspace holds the partial results
+ * of the splits each slice is cut into (and, for hx_decode_attn, the slice
+ * partials); it needs no initialisation and its contents are scratch
+ * between calls. */
 hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes);
 
 /* Zero a workspace (device) on `stream` (optional; for callers that want
@@ -210,6 +211,21 @@ hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream);
 hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
                                  const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* The whole decode step's attention in one call: the final O [B][Hq][Dv]
+ * (fp32, normalised) and natural-log LSE [B][Hq] of every query head over
+ * its request's full context, i.e. hx_decode_attn_partial followed by
+ * hx_lse_combine (Helix summary, paragraph on KV parallelism; jaehun.me
+ * review, Prompt 1.3.2), for callers that hold all slices on one GPU and do
+ * not need the per-slice partials.  Same arguments and checks as
+ * hx_decode_attn_partial, with o, lse (device, 16-byte aligned) in place of
+ * o_part, lse_part; the slice partials live in the workspace.  Two kernel
+ * launches: the partial pass, then one kernel that folds every slice's
+ * partial (or its split records) into the final output with the LSE rule,
+ * in place of the split fold and the combine. */
+hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                         const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* LSE-weighted combine of P partials (jaehun.me review, Prompt 1.3.2):
  *   m = max_r LSE_r, w_r = exp(LSE_r - m),

@@ -50,6 +50,7 @@ SIGNATURES = {
     "hx_workspace_size": (I32, [P_DESC, I32, ctypes.POINTER(SZ)]),
     "hx_workspace_init": (I32, [VP, SZ, VP]),
     "hx_decode_attn_partial": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_decode_attn": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_lse_combine": (I32, [I32, I32, I32, I32, VP, VP, VP, VP, VP]),
 }
 

@@ -160,6 +160,15 @@ def decode_attn_partial(cache: KVCache, q, ctx_len, scale, o_part, lse_part, ws,
                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def decode_attn(cache: KVCache, q, ctx_len, scale, o, lse, ws, stream=None):
+    """``hx_decode_attn``: q bf16 [B, Hq, Dk] -> o f32 [B, Hq, Dv], lse f32
+    [B, Hq] (the whole step; ws zeroed once before its first use here)."""
+    Hq = q.shape[1]
+    check(lib().hx_decode_attn(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq, _i64(ctx_len),
+                               float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)))
+
+
 def lse_combine(o_part, lse_part, o, lse, stream=None):
     """``hx_lse_combine``: o_part [P, B, Hq, Dv], lse_part [P, B, Hq] ->
     o [B, Hq, Dv], lse [B, Hq] (all float32)."""

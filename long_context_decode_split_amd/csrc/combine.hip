@@ -120,7 +120,73 @@ __global__ __launch_bounds__(kFoldThreads) void split_fold_kernel(const PartialA
     a.lse_part[((int64_t)r * a.Btot + b) * a.Hq + g * G + hd] = den > 0.f ? m + __log2f(den) * kLn2 : -INFINITY;
 }
 
+// hx_decode_attn's completion: one workgroup per (request, query head) of
+// the launch folds the partial of every (slice, split) of its group by the
+// same LSE rule, straight into the final output: for a slice with one split
+// the partial kernel wrote the slice output, otherwise the split records.
+constexpr int kFcThreads = 128;
+constexpr int kFcMaxItems = kMaxSplits * 64;   // P * nsplit (P <= 64)
+
+__global__ __launch_bounds__(kFcThreads) void fold_combine_kernel(const PartialArgs a, float* __restrict__ o,
+                                                                  float* __restrict__ lse) {
+  __shared__ float s_w[kFcMaxItems];
+  __shared__ float s_red[kFcThreads / 64];
+  const int G = a.G, Dv = a.Dv, P = a.P;
+  const int f = blockIdx.x;
+  const int bl = f / a.Hq;
+  const int hq = f % a.Hq;
+  const int g = hq / G, hd = hq % G;
+  const int b = a.b0 + bl;
+  const int nsplit = a.nsplit[bl];
+  const int items = P * nsplit;
+  const int64_t rec0 = a.wg_begin[bl] + (int64_t)g * P * nsplit;   // records of (request, KV head g), slice-major
+  const int tid = threadIdx.x;
+  auto item_lse = [&](int i) -> float {
+    return nsplit == 1 ? a.lse_part[((int64_t)i * a.Btot + b) * a.Hq + hq] : a.ws_lse[(rec0 + i) * G + hd];
+  };
+  auto item_o = [&](int i, int d) -> float {
+    return nsplit == 1 ? a.o_part[(((int64_t)i * a.Btot + b) * a.Hq + hq) * Dv + d]
+                       : a.ws_o[((rec0 + i) * G + hd) * Dv + d];
+  };
+  float m = -INFINITY;
+  for (int i = tid; i < items; i += kFcThreads) {
+    const float l = item_lse(i);
+    s_w[i] = l;
+    m = fmaxf(m, l);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kFcThreads / 64; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+  const bool empty = m == -INFINITY;
+  for (int i = tid; i < items; i += kFcThreads) s_w[i] = empty ? 0.f : __builtin_amdgcn_exp2f((s_w[i] - m) * kLog2e);
+  __syncthreads();
+  float den = 0.f;
+  for (int i = 0; i < items; ++i) den += s_w[i];
+  for (int d = tid; d < Dv; d += kFcThreads) {
+    float num = 0.f;
+    for (int i = 0; i < items; ++i) {
+      const float w = s_w[i];
+      if (w != 0.f) num += w * item_o(i, d);
+    }
+    o[((int64_t)b * a.Hq + hq) * Dv + d] = den > 0.f ? num / den : 0.f;
+  }
+  if (tid == 0) lse[(int64_t)b * a.Hq + hq] = den > 0.f ? m + __log2f(den) * kLn2 : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_fold_combine(const PartialArgs& a, float* o, float* lse, hipStream_t st) {
+  const int nf = a.nb * a.Hq;
+  if (nf == 0) return hipSuccess;
+  for (int i = 0; i < a.nb; ++i)
+    if (a.nsplit[i] * a.P > kFcMaxItems) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fold_combine_kernel, dim3(nf), dim3(kFcThreads), 0, st, a, o, lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_split_fold(const PartialArgs& a, hipStream_t st) {
   const int nf = a.fold_begin[a.nb];

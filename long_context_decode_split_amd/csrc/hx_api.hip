@@ -113,15 +113,20 @@ static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // Workspace: one record per workgroup of a launch, [records][G][Dv] partial
 // outputs then [records][G] LSEs.
 struct WsLayout {
-  int64_t o_off, lse_off, total;
+  int64_t o_off, lse_off;         // split records
+  int64_t opart_off, lpart_off;   // slice partials of hx_decode_attn
+  int64_t total;
 };
 
 static WsLayout ws_layout(const hx_kv_desc& d, int kind, int G) {
   WsLayout w;
   const int64_t recs = ws_records(d, kind);
+  const int64_t Hq = (int64_t)G * d.Hkv;
   w.o_off = 0;
   w.lse_off = align256(recs * G * d.Dv * 4);
-  w.total = w.lse_off + align256(recs * G * 4);
+  w.opart_off = w.lse_off + align256(recs * G * 4);
+  w.lpart_off = w.opart_off + align256((int64_t)d.P * d.B * Hq * d.Dv * 4);
+  w.total = w.lpart_off + align256((int64_t)d.P * d.B * Hq * 4);
   return w;
 }
 
@@ -388,11 +393,16 @@ hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return check_hip(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream), "workspace memset");
 }
 
-hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
-                                 const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
-                                 size_t ws_bytes, void* stream) {
+// The partial pass of a decode step.  With o_final / lse_final (hx_decode_attn)
+// the slice partials go to workspace scratch and one more kernel folds every
+// slice's partial or split records straight into the final output.
+static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                             const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                             size_t ws_bytes, void* stream, float* o_final, float* lse_final) {
   g_err[0] = 0;
-  if (!desc || !cache || !q || !ctx_len || !o_part || !lse_part || !ws) return fail(HX_EINVAL, "null argument");
+  const bool final_out = o_final != nullptr;
+  if (!desc || !cache || !q || !ctx_len || !ws) return fail(HX_EINVAL, "null argument");
+  if (final_out ? !lse_final : (!o_part || !lse_part)) return fail(HX_EINVAL, "null argument");
   Geometry geo;
   hx_status s = geometry(*desc, &geo);
   if (s) return s;
@@ -403,13 +413,18 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
   if (!cache->k || (!d.v_alias_k && !cache->v)) return fail(HX_EINVAL, "null cache plane");
   if (d.dtype != HX_KV_BF16 && (!cache->k_scale || (!d.v_alias_k && !cache->v_scale)))
     return fail(HX_EINVAL, "null scale plane");
-  const void* ptrs[8] = {cache->k, cache->v, cache->k_scale, cache->v_scale, q, o_part, lse_part, ws};
+  const void* ptrs[10] = {cache->k, cache->v, cache->k_scale, cache->v_scale, q, o_part, lse_part, ws,
+                          o_final, lse_final};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int G = Hq / d.Hkv;
   const WsLayout wl = ws_layout(d, geo.kind, G);
   if ((int64_t)ws_bytes < wl.total)
     return fail(HX_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)wl.total);
+  if (final_out) {
+    o_part = (float*)((uint8_t*)ws + wl.opart_off);
+    lse_part = (float*)((uint8_t*)ws + wl.lpart_off);
+  }
   const int64_t nmax = (int64_t)d.P * d.cap;
   for (int b = 0; b < d.B; ++b)
     if (ctx_len[b] < 1 || ctx_len[b] > nmax)
@@ -473,10 +488,27 @@ hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cach
                                  : launch_mla_partial(a, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
     if (s) return s;
-    s = check_hip(launch_split_fold(a, (hipStream_t)stream), "split fold launch");
+    s = final_out ? check_hip(launch_fold_combine(a, o_final, lse_final, (hipStream_t)stream), "fold/combine launch")
+                  : check_hip(launch_split_fold(a, (hipStream_t)stream), "split fold launch");
     if (s) return s;
   }
   return HX_OK;
+}
+
+hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                                 const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return decode_step(desc, cache, q, Hq, ctx_len, scale, o_part, lse_part, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                         const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!o) {
+    g_err[0] = 0;
+    return fail(HX_EINVAL, "null argument");
+  }
+  return decode_step(desc, cache, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
 }
 
 hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,

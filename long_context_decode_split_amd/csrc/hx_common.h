@@ -202,6 +202,11 @@ hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
 // slice outputs (o_part, lse_part); no-op when every slice has one split.
 hipError_t launch_split_fold(const PartialArgs& a, hipStream_t st);
 
+// hx_decode_attn's completion: folds every (slice, split) partial of each
+// (request, query head) - the slice outputs of one-split slices, the split
+// records of the others - into the final O and LSE in one pass.
+hipError_t launch_fold_combine(const PartialArgs& a, float* o, float* lse, hipStream_t st);
+
 hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part, const float* lse_part, float* o,
                               float* lse, hipStream_t st);
 

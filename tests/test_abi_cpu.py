@@ -187,6 +187,24 @@ def test_partial_argument_checks_return_before_launch():
     assert _partial(d, [5, 5], cache=_lib.hx_kv_cache(0x50000, None, None, None)) == _lib.HX_EINVAL
 
 
+def test_decode_attn_argument_checks():
+    L = _lib.lib()
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+    ctx = (ctypes.c_int64 * 2)(5, 17)
+
+    def call(o=0x30000, lse=0x40000, ws_bytes=1 << 30):
+        return L.hx_decode_attn(ctypes.byref(d.c()), ctypes.byref(cache), _fake(0x10000), 8, ctx, ctypes.c_float(0.1),
+                                _fake(o) if o else None, _fake(lse) if lse else None, _fake(0x20000), ws_bytes, None)
+
+    assert call(o=0) == _lib.HX_EINVAL
+    assert call(lse=0) == _lib.HX_EINVAL
+    assert call(o=0x30004) == _lib.HX_EINVAL     # misaligned
+    assert call(ws_bytes=16) == _lib.HX_EINVAL
+    if not torch.cuda.is_available():
+        assert call() == _lib.HX_EHIP             # valid arguments reach the launch
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_partial_without_device_is_hx_ehip():
     d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)

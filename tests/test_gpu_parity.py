@@ -300,6 +300,47 @@ def test_decode_step_append_then_attend():
     H.check_step(inp, o_part, lse_part, o, lse, label="append+attend")
 
 
+ONE_CALL_CASES = [
+    configs.TINY_GQA,
+    configs.TINY_GQA.scaled(B=3, Hkv=2, Hq=8, ctx=None, ctx_range=(1, 6000), P=4),
+    configs.FP8_GQA.scaled(B=2, ctx=None, ctx_range=(100, 9000)),
+    configs.MXFP4_RAGGED.scaled(B=2, ctx_range=(1, 9000)),
+    configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(20000, 60000)),      # many splits per slice
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4),
+]
+
+
+@pytest.mark.parametrize("w", ONE_CALL_CASES, ids=_ids)
+def test_decode_attn_whole_step(w):
+    """hx_decode_attn (partials, then one fold of every slice's partial or
+    split records into the final output) against the oracle's unsplit
+    attention; three calls on one workspace give identical bits."""
+    seed = 3 + len(_ids(w))
+    H.log(f"[one-call] {_ids(w)} seed={seed}")
+    inp = synth.make_inputs(w, seed, device=DEV, needles=True)
+    cache = H.build_cache(inp)
+    ws = torch.zeros(api.workspace_size(cache.desc, w.Hq), dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(3):
+        o = torch.full((w.B, w.Hq, w.Dv), float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((w.B, w.Hq), float("nan"), dtype=torch.float32, device=DEV)
+        api.decode_attn(cache, inp.q, inp.ctx, w.softmax_scale, o, lse, ws)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    o, lse = outs[0]
+    oc, lc = o.cpu().numpy(), lse.cpu().numpy()
+    worst = [0.0, 0.0]
+    for b, g in H.all_groups(inp):
+        heads = np.arange(w.G) if w.G <= 16 else np.array([0, 31, 32, 63, 64, 95, 96, 127])
+        _, _, O, L = H.oracle_group(inp, b, g, heads)
+        cols = g * w.G + heads
+        e = H.compare(f"{_ids(w)} b={b} g={g}", oc[b, cols], lc[b, cols], O, L, w.dtype)
+        worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
 @pytest.mark.parametrize("P", [1, 3, 8, 100])
 def test_lse_combine_matches_oracle(P):
     g = torch.Generator(device="cpu").manual_seed(P)
