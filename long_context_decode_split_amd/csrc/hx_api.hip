@@ -89,6 +89,8 @@ static int device_cus() {
   return cache[dev];
 }
 
+constexpr int64_t kShortSliceChunks = 64;   // 1,024 rows per slice
+
 int target_wgs(int kind, int dtype) {
   // Workgroups per CU for one launch, measured on MI355X at 1M-token contexts:
   // bf16 / fp8 tiles stream best with two workgroups per CU (one round, all
@@ -101,7 +103,14 @@ int target_wgs(int kind, int dtype) {
   return std::min(bound, device_cus() * per_cu);
 }
 
-int min_chunks_per_wg(int kind) { return kind == 0 ? 4 * kGqaWavesPerWg : 4; }
+// Smallest split (chunk tiles per workgroup): GQA waves each take one tile in
+// turn, so four per wave keep their loads pipelined; MLA tiles come in pairs.
+// HX_MIN_CHUNKS_PER_WG overrides (tuning knob).
+int min_chunks_per_wg(int kind) {
+  const int dflt = kind == 0 ? 4 * kGqaWavesPerWg : 4;
+  const int v = env_int("HX_MIN_CHUNKS_PER_WG", dflt, 1, 1 << 20);
+  return kind == 1 ? v + (v & 1) : v;
+}
 
 static int64_t ws_records(const hx_kv_desc& d, int kind) {
   const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
@@ -469,6 +478,10 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, c
     for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
     int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
     cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
+    // short contexts: slices of at most kShortSliceChunks tiles are not split
+    // (one workgroup per slice, no fold launch; measured faster on the
+    // 4,096-token single-request step, where fixed launch costs dominate)
+    if (nch_max <= kShortSliceChunks) cpw = std::max<int64_t>(cpw, nch_max);
     if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
     a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
     int wgs = 0, folds = 0;
