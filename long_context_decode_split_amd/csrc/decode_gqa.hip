@@ -23,7 +23,8 @@
 //     lane exchanges and the running sum stays per lane;
 //   * O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16, whose B operand is
 //     the probability fragment exactly as the first product left it.
-// The per-head rescale of the accumulator runs only when some head's max grew.
+// The rescale of the accumulator runs only on tiles that move a head's
+// reference max (bf16: any growth; fp8 / MXFP4: growth by more than 2^8).
 
 #include "hx_common.h"
 
@@ -42,14 +43,26 @@ constexpr int kWaves = kGqaWavesPerWg;
 #ifndef HX_GQA_TILES_BF16
 #define HX_GQA_TILES_BF16 2
 #endif
-#ifndef HX_GQA_TILES_Q
-#define HX_GQA_TILES_Q 3
+#ifndef HX_GQA_TILES_FP8
+#define HX_GQA_TILES_FP8 3
+#endif
+#ifndef HX_GQA_TILES_FP4
+#define HX_GQA_TILES_FP4 3
 #endif
 template <int FMT>
-constexpr int kTilesInFlight = FMT == 0 ? HX_GQA_TILES_BF16 : HX_GQA_TILES_Q;
+constexpr int kTilesInFlight = FMT == 0 ? HX_GQA_TILES_BF16 : (FMT == 1 ? HX_GQA_TILES_FP8 : HX_GQA_TILES_FP4);
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr float kLn2 = 0.693147180559945309f;
+// log2 of the largest unnormalised probability (see chunk_step).  bf16
+// caches keep the reference at the running max (P <= 1, and the rows at the
+// max get the exact weight 1); the quantised formats, whose dequantisation
+// leaves less VALU time per tile, let it lag by up to 2^8.
+#ifndef HX_GQA_HEADROOM_Q
+#define HX_GQA_HEADROOM_Q 8.0f
+#endif
+template <int FMT>
+constexpr float kHeadroom = FMT == 0 ? 0.0f : HX_GQA_HEADROOM_Q;
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
@@ -73,8 +86,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // fp8 e4m3 byte pairs -> packed bf16 (exact: e4m3 values are bf16 values).
 template <bool HI>
@@ -92,7 +103,42 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
 // shift, no branch.  Exact for E = 1..254; E = 0 (2^-127, elements below
 // 3.6e-38 in magnitude) reads as 0 and E = 255 (NaN) as +inf, so such blocks
 // give zero resp. non-finite contributions.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+// Byte J of w is taken through a sub-dword operand select of the shift, so
+// the conversion is one instruction.
+template <int J>
+__device__ __forceinline__ float e8m0_byte(uint32_t w) {
+  uint32_t r;
+  if constexpr (J == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(23u), "v"(w));
+  else if constexpr (J == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(23u), "v"(w));
+  else if constexpr (J == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(23u), "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(23u), "v"(w));
+  return __uint_as_float(r);
+}
+
+// Byte j (a constant after unrolling) of w as 2^(byte - 127).
+__device__ __forceinline__ float e8m0_sel(uint32_t w, int j) {
+  switch (j) {
+    case 0: return e8m0_byte<0>(w);
+    case 1: return e8m0_byte<1>(w);
+    case 2: return e8m0_byte<2>(w);
+    default: return e8m0_byte<3>(w);
+  }
+}
+
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// c + (sum of a packed bf16 pair), in fp32.
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), kOnes2, c, false);
+}
 
 // Raw bytes of one chunk tile that a lane needs; FMT 0 bf16, 1 fp8, 2 MXFP4.
 template <int FMT>
@@ -182,7 +228,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
     const uint32_t w[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float sc = e8m0_to_f32((cur.ksc >> (8 * s)) & 0xff);
+      const float sc = e8m0_sel(cur.ksc, s);
       uint4 t;
       t.x = fp4x2_to_bf16x2<0>(w[s], sc);
       t.y = fp4x2_to_bf16x2<1>(w[s], sc);
@@ -210,15 +256,20 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   cm = fmaxf(cm, __shfl_xor(cm, 16));
   cm = fmaxf(cm, __shfl_xor(cm, 32));
-  // Rescale unconditionally (alpha = 1 when the max did not grow): a branch
-  // here would cost more in register copies than the 32 multiplies.
-  const float mnew = fmaxf(st.mrun, cm * cscale);
-  const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
+  // The reference max mrun moves only when some head's scores exceed it by
+  // more than kHeadroom: P = 2^(s - mrun) is bounded by 2^kHeadroom, and the
+  // rescale of the accumulator (32 multiplies; a factor of exactly 1 for the
+  // heads whose max did not move) runs only on the tiles that raise it.
+  const float cms = cm * cscale;
+  if (__any(cms > st.mrun + kHeadroom<FMT>)) {   // wave-uniform
+    const float mnew = fmaxf(st.mrun, cms);
+    const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.acc[i] *= alpha;
-  st.lsum_mfma *= alpha;
-  st.lsum *= alpha;
-  st.mrun = mnew;
+    for (int i = 0; i < 8; ++i) st.acc[i] *= alpha;
+    st.lsum_mfma *= alpha;
+    st.lsum *= alpha;
+    st.mrun = mnew;
+  }
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -st.mrun));
@@ -227,7 +278,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
   if constexpr (FMT == 0) {
     const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-    st.lsum_mfma += (bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23));
+    st.lsum_mfma = add_bf16x2(p23, add_bf16x2(p01, st.lsum_mfma));
     const s16x4 pb = as_s16x4(p01, p23);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -242,7 +293,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
     // the scale, are what normalises O.
     const float vsc = cur.vs;
     const uint32_t p01 = pack_bf16(p[0] * vsc, p[1] * vsc), p23 = pack_bf16(p[2] * vsc, p[3] * vsc);
-    st.lsum_mfma += ((bf16lo(p01) + bf16hi(p01)) + (bf16lo(p23) + bf16hi(p23))) * (1.0f / vsc);
+    st.lsum_mfma = fmaf(add_bf16x2(p23, add_bf16x2(p01, 0.f)), __builtin_amdgcn_rcpf(vsc), st.lsum_mfma);
     const s16x4 pb = as_s16x4(p01, p23);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -256,17 +307,18 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
     }
   } else {
     // Per (token, 32-column block) scales are powers of two: fold them into
-    // P (exact), one P fragment per block.
+    // P, one P fragment per block.  Scaling by a power of two commutes with
+    // the rounding to bf16 (outside the subnormal range), so the sum of the
+    // rounded, unscaled P is what normalises O.
     const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-    const float pr[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
-    st.lsum_mfma += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    st.lsum_mfma = add_bf16x2(p23, add_bf16x2(p01, st.lsum_mfma));
     const uint32_t vs[4] = {cur.vsc.x, cur.vsc.y, cur.vsc.z, cur.vsc.w};   // token 4h+j: 4 block scales
     const uint32_t w[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       float ps[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ps[j] = pr[j] * e8m0_to_f32((vs[j] >> (8 * blk)) & 0xff);
+      for (int j = 0; j < 4; ++j) ps[j] = p[j] * e8m0_sel(vs[j], blk);
       if constexpr (TAIL) {   // rows past the slice end may hold any scale byte
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -343,9 +395,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
   st.lsum = 0.f;
 
   const float c2 = a.c2;
-  auto load = [&](Frag<FMT>& f, int c) {
-    f.load(kp + (int64_t)c * a.k_tile, vp + (int64_t)c * a.v_tile, ksp ? ksp + (int64_t)c * a.ks_tile : nullptr,
-           vsp ? vsp + (int64_t)c * a.vs_tile : nullptr, lane, 0);
+  // Tile c of the slice lies at kp + c * k_tile (and likewise for V and the
+  // scales).  Loads go through byte cursors that hold wave-uniform offsets,
+  // so addresses are a scalar base plus the lane's 16-byte offset.
+  auto load_at = [&](Frag<FMT>& f, int64_t ok, int64_t ov, int64_t oks, int64_t ovs) {
+    if constexpr (FMT == 0)
+      f.load(kp + ok, vp + ov, nullptr, nullptr, lane, 0);
+    else
+      f.load(kp + ok, vp + ov, ksp + oks, vsp + ovs, lane, 0);
   };
   // The slice's partial last tile (if this split holds it) is taken out of
   // the streaming loop and done once at the end, so the loop has no branch.
@@ -356,21 +413,36 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
   // registers of the tile just consumed.  The steady-state loop issues its
   // loads unconditionally so the wait counts stay exact (the wave keeps the
   // other tiles' loads in flight while it computes); the last tiles are
-  // drained after it.
+  // drained after it.  A wave takes chunks c0 + wave, + kWaves, ... in order,
+  // so one cursor advanced by kWaves tiles per load covers all its loads.
   constexpr int NBUF = kTilesInFlight<FMT>;
-  const int first = c0 + wave;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int first = c0 + wv;
   const int nmine = __builtin_amdgcn_readfirstlane(first < c1f ? (c1f - first + kWaves - 1) / kWaves : 0);
   if (nmine > 0) {
-    auto chunk = [&](int i) { return first + i * kWaves; };
+    int64_t ok = (int64_t)first * a.k_tile, ov = (int64_t)first * a.v_tile;
+    int64_t oks = (int64_t)first * a.ks_tile, ovs = (int64_t)first * a.vs_tile;
+    const int64_t dk = (int64_t)kWaves * a.k_tile, dv = (int64_t)kWaves * a.v_tile;
+    const int64_t dks = (int64_t)kWaves * a.ks_tile, dvs = (int64_t)kWaves * a.vs_tile;
+    auto load_next = [&](Frag<FMT>& f, bool advance) {
+      load_at(f, ok, ov, oks, ovs);
+      if (advance) {
+        ok += dk;
+        ov += dv;
+        oks += dks;
+        ovs += dvs;
+      }
+    };
     Frag<FMT> f[NBUF];
+    // with fewer than NBUF tiles the cursor stays on the last one
 #pragma unroll
-    for (int k = 0; k < NBUF; ++k) load(f[k], chunk(k < nmine ? k : nmine - 1));
+    for (int k = 0; k < NBUF; ++k) load_next(f[k], k + 1 < nmine);
     int i = 0;
     for (; i + 2 * NBUF - 1 < nmine; i += NBUF) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
         chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
-        load(f[k], chunk(i + k + NBUF));
+        load_next(f[k], true);
 #if HX_GQA_SCHED_BARRIER
         __builtin_amdgcn_sched_barrier(0);   // keep the next tile's math below this reload
 #endif
@@ -380,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     for (int k = 0; k < NBUF; ++k) {
       if (i + k < nmine) {
         chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
-        if (i + k + NBUF < nmine) load(f[k], chunk(i + k + NBUF));
+        if (i + k + NBUF < nmine) load_next(f[k], true);
       }
     }
 #pragma unroll
@@ -388,8 +460,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
       if (i + NBUF + k < nmine) chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
   }
   if (has_tail && wave == (c1 - 1 - c0) % kWaves) {
+    const int64_t c = c1 - 1;
     Frag<FMT> t;
-    load(t, c1 - 1);
+    load_at(t, c * a.k_tile, c * a.v_tile, c * a.ks_tile, c * a.vs_tile);
     chunk_step<FMT, true>(t, st, qf, c2, h, tail_valid);
   }
   float mrun = st.mrun, lsum = st.lsum, lsum_mfma = st.lsum_mfma;

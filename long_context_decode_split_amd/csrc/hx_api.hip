@@ -94,10 +94,12 @@ constexpr int64_t kShortSliceChunks = 64;   // 1,024 rows per slice
 int target_wgs(int kind, int dtype) {
   // Workgroups per CU for one launch, measured on MI355X at 1M-token contexts:
   // bf16 / fp8 tiles stream best with two workgroups per CU (one round, all
-  // resident); MXFP4 tiles carry more dequantisation work per byte and gain
-  // from more waves.  The MLA kernel holds 152 KiB of LDS: one workgroup of
-  // eight waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
-  const int dflt = kind != 0 ? 1 : (dtype == HX_KV_MXFP4 ? 4 : 2);
+  // resident); MXFP4 splits are short in time (a quarter of the bf16 bytes
+  // per row) and three workgroups fit per CU, so eight per CU keep the
+  // rounds even (measured: 475 us at four, 445 us at eight on the ragged
+  // 16-request cache).  The MLA kernel holds 152 KiB of LDS: one workgroup
+  // of eight waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
+  const int dflt = kind != 0 ? 1 : (dtype == HX_KV_MXFP4 ? 8 : 2);
   const int per_cu = env_int("HX_WGS_PER_CU", dflt, 1, 8);
   const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
   return std::min(bound, device_cus() * per_cu);

@@ -124,7 +124,10 @@ def _store(x, dtype):
     return _quant_mxfp4(x)
 
 
-def make_inputs(w: Workload, seed: int = 0, device="cuda", needles: bool = False) -> Inputs:
+def make_inputs(w: Workload, seed: int = 0, device="cuda", needles: bool = False, plant=None) -> Inputs:
+    """Seeded inputs of workload w.  `plant(b, kb, q)`, if given, may edit the
+    fp32 K rows kb [Hkv, n, Dk] of request b (before they are stored in the
+    cache format), e.g. to set rows with chosen scores."""
     ctx = context_lengths(w, seed)
     nmax = max(ctx)
     cap = capacity(ctx, w.P)
@@ -165,6 +168,8 @@ def make_inputs(w: Workload, seed: int = 0, device="cuda", needles: bool = False
                     alpha = target / (w.softmax_scale * float(qh.norm()))
                     kb[gg, ts] = (alpha * qh / qh.norm())[None, :]
             needle_map[b] = pos
+        if plant is not None:
+            plant(b, kb, q)
         kc, kscale = _store(kb, w.dtype)
         k[b, :, :n] = kc
         if ks is not None:

@@ -263,6 +263,42 @@ def test_mla_large_score_jumps(staircase):
     H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
 
 
+@pytest.mark.parametrize("staircase", [False, True], ids=["one-jump", "staircase"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3", "mxfp4"])
+def test_gqa_score_jumps(dtype, staircase):
+    """Rows whose scores rise far above everything before them, late in a
+    split: the GQA kernel moves a head's softmax reference only when a tile
+    raises it (bf16) or raises it by more than 2^8 (fp8, MXFP4), so jumps
+    both below and above that margin are planted.  Rows aligned with one
+    head's query get natural-log scores of 3-60; the staircase raises the
+    same heads four times within one split."""
+    w = configs.LLAMA405B_SHARE.scaled(B=1, ctx=200000, P=2, dtype=dtype)
+
+    def plant(b, kb, q):
+        def put(j, r, h, target):
+            t = _slice_row_to_token(j, r, w.P)
+            qh = q[b, h].float()
+            alpha = target / (w.softmax_scale * float(qh.norm()))
+            kb[0, t] = alpha * qh / qh.norm()
+
+        if staircase:
+            for r, h in ((0, 0), (1, 9), (0, 15)):
+                for j, target in ((100, 3.0), (300, 6.0), (700, 20.0), (5000, 60.0)):
+                    put(j + h, r, h, target)
+        else:
+            for i, (j, r) in enumerate(((40, 0), (1000, 1), (1530, 0), (22100, 1), (3000, 0), (60000, 1))):
+                put(j, r, (0, 4, 7, 11, 13, 15)[i], (4.0, 8.0, 30.0, 60.0, 5.0, 45.0)[i])
+
+    H.log(f"[gqa jumps] {dtype} staircase={staircase}")
+    inp = synth.make_inputs(w, 23, device=DEV, plant=plant)
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label=f"gqa jumps {dtype} staircase={staircase}")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
 def test_partials_are_deterministic_and_workspace_reusable():
     w = configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(5000, 60000))
     inp = synth.make_inputs(w, 4, device=DEV)
