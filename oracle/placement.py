@@ -57,3 +57,28 @@ def slice_len(n: int, P: int, r: int) -> int:
     mine = left - CHUNK * r
     mine = 0 if mine < 0 else (CHUNK if mine > CHUNK else mine)
     return full_rounds * CHUNK + mine
+
+
+# ---------------------------------------------------------------------------
+# Block-pool (paged) storage of the same placement.
+#
+# The pages fix where a token goes (slice, arrival order) but not how a
+# slice's rows are stored.  A serving cache that grows per request keeps each
+# slice as a list of 16-row blocks taken from a shared pool (the 16-token
+# group is the placement unit: Helix summary, paragraph on Helix's two
+# layouts; the stated goal of the rotation is an even memory fill).  Reading:
+# local row j of slice r of request b lives in block table[b][r][j // 16],
+# row j % 16 of that block.
+
+
+def blocks_needed(n: int, P: int, r: int) -> int:
+    """Blocks slice ``r`` occupies when the request has ``n`` tokens: the
+    distinct 16-row groups among its rows (found by enumeration)."""
+    return len({j // CHUNK for j in (slot(t, P)[1] for t in range(n) if slot(t, P)[0] == r)})
+
+
+def block_row(t: int, P: int, table_b):
+    """(block id, row inside the block) of token ``t`` of a request whose
+    per-slice block lists are ``table_b[r][c]``."""
+    r, j = slot(t, P)
+    return table_b[r][j // CHUNK], j % CHUNK

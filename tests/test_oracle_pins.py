@@ -249,6 +249,36 @@ def test_slice_len_examples():
     assert placement.slice_len(1 << 20, 8, 5) == 131072
 
 
+def test_blocks_needed_is_the_ceiling_of_the_slice_rows():
+    for P in (1, 2, 3, 8):
+        for n in list(range(0, 16 * P * 3 + 5)) + [4137]:
+            for r in range(P):
+                assert placement.blocks_needed(n, P, r) == -(-placement.slice_len(n, P, r) // 16), (n, P, r)
+
+
+def test_block_rows_are_a_bijection_onto_the_listed_blocks():
+    """Every token of a request lands on its own (block, row); the blocks in
+    use are exactly the first blocks_needed entries of each slice's list;
+    tokens of one 16-token group share a block in arrival order."""
+    rng = np.random.default_rng(7)
+    for P in (1, 2, 5, 8):
+        for n in (1, 15, 16, 17, 16 * P, 16 * P + 1, 700, 4137):
+            nb = [placement.blocks_needed(n, P, r) for r in range(P)]
+            ids = rng.permutation(sum(nb) + 11)          # a pool with spare blocks, shuffled
+            table, k = [], 0
+            for r in range(P):
+                table.append(list(ids[k:k + nb[r]]) + [-1] * 3)
+                k += nb[r]
+            where = [placement.block_row(t, P, table) for t in range(n)]
+            assert len(set(where)) == n
+            assert all(blk >= 0 and 0 <= row < 16 for blk, row in where)
+            used = {blk for blk, _ in where}
+            assert used == {table[r][c] for r in range(P) for c in range(nb[r])}
+            for t in range(n):
+                g0 = (t // 16) * 16
+                assert where[t] == (where[g0][0], t - g0)
+
+
 # ---------------------------------------------------------------- codecs
 
 def _spec_value(v):
