@@ -49,7 +49,8 @@ typedef enum {
   HX_OK = 0,
   HX_EINVAL = 1,       /* bad argument (null, misaligned, out of range) */
   HX_EUNSUPPORTED = 2, /* valid but not implemented (shape / dtype combo) */
-  HX_EHIP = 3          /* the HIP runtime reported an error */
+  HX_EHIP = 3,         /* the HIP runtime reported an error */
+  HX_ENOSPC = 4        /* a block pool has too few free blocks */
 } hx_status;
 
 typedef enum {
@@ -235,6 +236,94 @@ hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const
  * LSE_r = -inf) give o = 0, lse = -inf.  1 <= P <= 1024. */
 hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,
                          float* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block-pool (paged) caches
+ *
+ * The same placement (hx_slot) with a different storage: instead of a
+ * [P][B][Hkv][cap/16] plane sized for the longest request, every slice of
+ * every request is a list of 16-row blocks taken from one shared pool, so
+ * requests grow independently and memory follows the tokens actually held
+ * (the 16-token group is the placement unit and an even memory fill is what
+ * the rotation is for: Helix summary, paragraph on Helix's two layouts).
+ *
+ * A block holds the 16-row chunk tiles of all Hkv KV heads for one (request,
+ * slice, 16-row group).  Planes of a pool of N blocks (device, caller-owned,
+ * sizes from hx_pool_layout):
+ *   k, v       : [N][Hkv] chunk tiles, tile byte order as in the dense cache;
+ *   k_scale,   : fp8: float [N][Hkv]; MXFP4: uint8 e8m0 [N][Hkv][16][D/32];
+ *   v_scale      bf16: NULL.  v and v_scale are NULL when v_alias_k = 1.
+ * block_table: device int32 [B][P][cap/16].  Entry (b, r, c) is the block
+ *   holding local rows 16c .. 16c+15 of slice r of request b.  desc->cap is
+ *   the longest slice a table row can describe (16 entries' worth of rows
+ *   per entry), so contexts still satisfy ctx <= P * cap.  Every entry a call
+ *   reads or writes (the groups of the rows it touches) must hold a block id
+ *   in [0, N), and distinct (b, r, c) in use must hold distinct blocks; ids
+ *   outside [0, N) are clamped into it on the device (wrong rows, never an
+ *   access outside the planes).  Entries of groups past a slice's rows are
+ *   never read.  hx_block_pool_* below maintain such a table on the host.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  hx_kv_cache planes;          /* k, v, k_scale, v_scale of the pool */
+  const int32_t* block_table;  /* device [B][P][cap/16] */
+  int32_t num_blocks;          /* N >= 1 */
+  int32_t reserved;            /* must be 0 */
+} hx_kv_pool;
+
+/* Plane sizes of a pool of num_blocks blocks for `desc` (host only);
+ * n_max = P * cap, the longest context the block table can describe. */
+hx_status hx_pool_layout(const hx_kv_desc* desc, int32_t num_blocks, hx_kv_layout_info* out);
+
+/* hx_kv_append, hx_kv_append_bf16 and hx_kv_dequant on a pool cache: same
+ * arguments, placement, encoding and errors, with the rows addressed through
+ * the block table (HX_EINVAL also for a null or misaligned table or
+ * num_blocks < 1). */
+hx_status hx_kv_append_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new, const void* v_new,
+                             const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
+                             const int32_t* count, int32_t n_new, void* stream);
+hx_status hx_kv_append_bf16_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new,
+                                  const void* v_new, const int64_t* pos, const int32_t* count, int32_t n_new,
+                                  void* stream);
+hx_status hx_kv_dequant_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, int32_t r, int32_t b, int32_t g,
+                              int64_t j0, int64_t n, float* k_out, float* v_out, void* stream);
+
+/* hx_decode_attn_partial and hx_decode_attn on a pool cache (same
+ * arguments, outputs, workspace and errors).  The kernels are the dense
+ * ones with tile addresses taken from the block table, so for equal rows
+ * the results are bit-identical to the dense cache's. */
+hx_status hx_decode_attn_partial_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,
+                                       const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                                       size_t ws_bytes, void* stream);
+hx_status hx_decode_attn_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,
+                               const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Host-side block allocator for a pool of num_blocks blocks: a free list
+ * that hands out the most recently freed block first (initially 0, 1, ...).
+ * The handle is an opaque host object; calls on one handle are serialised
+ * internally.  The tables it edits are host arrays int32 [B][P][cap/16] in
+ * the layout of hx_kv_pool.block_table, with -1 marking an entry without a
+ * block; the caller copies them to the device table. */
+typedef struct hx_block_pool hx_block_pool;
+
+hx_status hx_block_pool_create(int32_t num_blocks, hx_block_pool** out);
+void hx_block_pool_destroy(hx_block_pool* pool);
+hx_status hx_block_pool_free_count(const hx_block_pool* pool, int32_t* n_free);
+
+/* Make request b's lists cover a context of n tokens: every entry (b, r, c)
+ * with c < ceil(hx_slice_len(n, P, r) / 16) that holds -1 gets a free block;
+ * entries already holding a block keep it (each must be a block handed to
+ * request b, else HX_EINVAL).  All or nothing: with too few free blocks
+ * nothing changes and HX_ENOSPC is returned.  *n_taken (may be NULL)
+ * receives the number of blocks handed out.  0 <= n <= P * cap. */
+hx_status hx_block_pool_reserve(hx_block_pool* pool, const hx_kv_desc* desc, int32_t* table_host, int32_t b,
+                                int64_t n, int32_t* n_taken);
+
+/* Return every block of request b's lists to the pool and set its entries to
+ * -1 (a finished request).  An entry (other than -1) that is not a block
+ * handed to request b, or a block listed twice, is HX_EINVAL and leaves the
+ * pool and the table unchanged. */
+hx_status hx_block_pool_release(hx_block_pool* pool, const hx_kv_desc* desc, int32_t* table_host, int32_t b);
 
 #ifdef __cplusplus
 }

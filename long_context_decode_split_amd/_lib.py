@@ -7,9 +7,9 @@ import torch  # noqa: F401  (loads torch's HIP runtime first, so the library bin
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhelixdecode.so")
 
-HX_OK, HX_EINVAL, HX_EUNSUPPORTED, HX_EHIP = 0, 1, 2, 3
+HX_OK, HX_EINVAL, HX_EUNSUPPORTED, HX_EHIP, HX_ENOSPC = 0, 1, 2, 3, 4
 HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4 = 0, 1, 2
-STATUS_NAMES = {0: "HX_OK", 1: "HX_EINVAL", 2: "HX_EUNSUPPORTED", 3: "HX_EHIP"}
+STATUS_NAMES = {0: "HX_OK", 1: "HX_EINVAL", 2: "HX_EUNSUPPORTED", 3: "HX_EHIP", 4: "HX_ENOSPC"}
 
 
 class hx_kv_desc(ctypes.Structure):
@@ -29,7 +29,13 @@ class hx_kv_layout_info(ctypes.Structure):
                 ("v_tile_bytes", ctypes.c_size_t), ("n_max", ctypes.c_int64)]
 
 
+class hx_kv_pool(ctypes.Structure):
+    _fields_ = [("planes", hx_kv_cache), ("block_table", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 P_DESC = ctypes.POINTER(hx_kv_desc)
+P_POOL = ctypes.POINTER(hx_kv_pool)
 P_CACHE = ctypes.POINTER(hx_kv_cache)
 VP = ctypes.c_void_p
 I32, I64, F32, SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -52,6 +58,17 @@ SIGNATURES = {
     "hx_decode_attn_partial": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_decode_attn": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_lse_combine": (I32, [I32, I32, I32, I32, VP, VP, VP, VP, VP]),
+    "hx_pool_layout": (I32, [P_DESC, I32, ctypes.POINTER(hx_kv_layout_info)]),
+    "hx_kv_append_paged": (I32, [P_DESC, P_POOL, VP, VP, VP, VP, P_I64, P_I32, I32, VP]),
+    "hx_kv_append_bf16_paged": (I32, [P_DESC, P_POOL, VP, VP, P_I64, P_I32, I32, VP]),
+    "hx_kv_dequant_paged": (I32, [P_DESC, P_POOL, I32, I32, I32, I64, I64, VP, VP, VP]),
+    "hx_decode_attn_partial_paged": (I32, [P_DESC, P_POOL, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_decode_attn_paged": (I32, [P_DESC, P_POOL, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_block_pool_create": (I32, [I32, ctypes.POINTER(VP)]),
+    "hx_block_pool_destroy": (None, [VP]),
+    "hx_block_pool_free_count": (I32, [VP, P_I32]),
+    "hx_block_pool_reserve": (I32, [VP, P_DESC, P_I32, I32, I64, P_I32]),
+    "hx_block_pool_release": (I32, [VP, P_DESC, P_I32, I32]),
 }
 
 _lib = None

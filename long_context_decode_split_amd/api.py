@@ -9,14 +9,16 @@ PyTorch provides device memory and the current stream, nothing else.
 import ctypes
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from ._lib import (HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXError, check, hx_kv_cache, hx_kv_desc,
-                   hx_kv_layout_info, lib)
+                   hx_kv_layout_info, hx_kv_pool, lib)
 
-__all__ = ["HXError", "KVDesc", "KVCache", "DTYPES", "kv_layout", "slot", "slice_len", "kv_tile_offset", "kv_append",
-           "kv_dequant", "workspace_size", "workspace_init", "decode_attn_partial", "lse_combine", "version",
-           "exported_symbols"]
+__all__ = ["HXError", "KVDesc", "KVCache", "KVPool", "DTYPES", "kv_layout", "pool_layout", "slot", "slice_len",
+           "kv_tile_offset", "kv_append", "kv_append_bf16", "kv_dequant", "kv_append_paged", "kv_append_bf16_paged",
+           "kv_dequant_paged", "workspace_size", "workspace_init", "decode_attn_partial", "decode_attn",
+           "decode_attn_partial_paged", "decode_attn_paged", "lse_combine", "version", "exported_symbols"]
 
 DTYPES = {"bf16": HX_KV_BF16, "fp8_e4m3": HX_KV_FP8_E4M3, "mxfp4": HX_KV_MXFP4}
 
@@ -117,6 +119,84 @@ class KVCache:
         return sum(t.numel() for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None)
 
 
+def pool_layout(desc: KVDesc, num_blocks):
+    info = hx_kv_layout_info()
+    check(lib().hx_pool_layout(ctypes.byref(desc.c()), int(num_blocks), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in hx_kv_layout_info._fields_}
+
+
+class KVPool:
+    """A block-pool cache of one layer: planes of ``num_blocks`` blocks
+    (torch, sizes from ``hx_pool_layout``), the host block table (numpy int32
+    [B, P, cap/16], -1 = no block) that the library's host allocator
+    (``hx_block_pool_*``) edits, and its device copy ``table``, refreshed by
+    ``sync()``.  ``desc.cap`` bounds the rows a slice can list."""
+
+    def __init__(self, desc: KVDesc, num_blocks, device="cuda", fill=None):
+        self.desc = desc
+        self.num_blocks = int(num_blocks)
+        self.layout = lay = pool_layout(desc, num_blocks)
+
+        def plane(nbytes):
+            if nbytes == 0:
+                return None
+            t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            return t
+
+        self.k = plane(lay["k_bytes"])
+        self.v = plane(lay["v_bytes"])
+        self.k_scale = plane(lay["k_scale_bytes"])
+        self.v_scale = plane(lay["v_scale_bytes"])
+        self.table_host = np.full((desc.B, desc.P, desc.cap // 16), -1, dtype=np.int32)
+        self.table = torch.full(self.table_host.shape, -1, dtype=torch.int32, device=device)
+        handle = ctypes.c_void_p()
+        check(lib().hx_block_pool_create(self.num_blocks, ctypes.byref(handle)))
+        self._handle = handle
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value:
+            lib().hx_block_pool_destroy(h)
+            self._handle = None
+
+    def _table_ptr(self):
+        return self.table_host.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def reserve(self, b, n):
+        """``hx_block_pool_reserve``: request b's lists cover n tokens; returns
+        the number of blocks taken (host table only: call ``sync``)."""
+        taken = ctypes.c_int32()
+        check(lib().hx_block_pool_reserve(self._handle, ctypes.byref(self.desc.c()), self._table_ptr(), int(b), int(n),
+                                          ctypes.byref(taken)))
+        return taken.value
+
+    def release(self, b):
+        """``hx_block_pool_release``: every block of request b back to the pool."""
+        check(lib().hx_block_pool_release(self._handle, ctypes.byref(self.desc.c()), self._table_ptr(), int(b)))
+
+    def free_blocks(self):
+        n = ctypes.c_int32()
+        check(lib().hx_block_pool_free_count(self._handle, ctypes.byref(n)))
+        return n.value
+
+    def sync(self):
+        """Copy the host table to the device table (ordered on the current stream)."""
+        self.table.copy_(torch.from_numpy(self.table_host))
+
+    def c(self):
+        planes = hx_kv_cache(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale))
+        return hx_kv_pool(planes, _ptr(self.table), self.num_blocks, 0)
+
+    def nbytes(self):
+        return sum(t.numel() for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None)
+
+
+def _count(count):
+    return None if count is None else (ctypes.c_int32 * len(count))(*[int(c) for c in count])
+
+
 def kv_append(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, pos, count=None, stream=None):
     """``hx_kv_append``: token-major storage-format tensors of shape
     [B, Hkv, n_new, ...]; ``pos`` (and ``count``) are host sequences of B ints."""
@@ -139,6 +219,24 @@ def kv_append_bf16(cache: KVCache, k_new, v_new, pos, count=None, stream=None):
 def kv_dequant(cache: KVCache, r, b, g, j0, n, k_out, v_out=None, stream=None):
     check(lib().hx_kv_dequant(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), r, b, g, j0, n, _ptr(k_out),
                               _ptr(v_out), _stream(stream)))
+
+
+def kv_append_paged(pool: KVPool, k_new, v_new, k_scale_new, v_scale_new, pos, count=None, stream=None):
+    """``hx_kv_append_paged``: ``kv_append`` into a block pool."""
+    check(lib().hx_kv_append_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_scale_new), _ptr(v_scale_new), _i64(pos), _count(count), k_new.shape[2],
+                                   _stream(stream)))
+
+
+def kv_append_bf16_paged(pool: KVPool, k_new, v_new, pos, count=None, stream=None):
+    """``hx_kv_append_bf16_paged``: ``kv_append_bf16`` into a block pool."""
+    check(lib().hx_kv_append_bf16_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(k_new),
+                                        _ptr(v_new), _i64(pos), _count(count), k_new.shape[2], _stream(stream)))
+
+
+def kv_dequant_paged(pool: KVPool, r, b, g, j0, n, k_out, v_out=None, stream=None):
+    check(lib().hx_kv_dequant_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), r, b, g, j0, n,
+                                    _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 def workspace_size(desc: KVDesc, Hq):
@@ -167,6 +265,20 @@ def decode_attn(cache: KVCache, q, ctx_len, scale, o, lse, ws, stream=None):
     check(lib().hx_decode_attn(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq, _i64(ctx_len),
                                float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)))
+
+
+def decode_attn_partial_paged(pool: KVPool, q, ctx_len, scale, o_part, lse_part, ws, stream=None):
+    """``hx_decode_attn_partial_paged``: ``decode_attn_partial`` on a block pool."""
+    check(lib().hx_decode_attn_partial_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                             q.shape[1], _i64(ctx_len), float(scale), _ptr(o_part), _ptr(lse_part),
+                                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_attn_paged(pool: KVPool, q, ctx_len, scale, o, lse, ws, stream=None):
+    """``hx_decode_attn_paged``: ``decode_attn`` on a block pool."""
+    check(lib().hx_decode_attn_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(q), q.shape[1],
+                                     _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def lse_combine(o_part, lse_part, o, lse, stream=None):

@@ -343,7 +343,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
 }
 
-template <int FMT>
+template <int FMT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -368,7 +368,11 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
   const int c1 = min(c0 + a.cpw, nch);
   const int tail_valid = (int)(L - (int64_t)(nch - 1) * kChunk);   // rows in the last chunk
 
-  const int64_t tile0 = ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
+  // Dense cache: the slice's tiles are consecutive from tile0.  Block pool:
+  // chunk c is the tile of head g in block trow[c] (tile_of in hx_common.h).
+  const int64_t tile0 = PAGED ? 0 : ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
+  const int32_t* trow = PAGED ? a.table + ((int64_t)b * a.P + r) * a.cap_chunks : nullptr;
+  auto pool_tile = [&](int c) -> int64_t { return clamp_block(trow[c], a.num_blocks) * a.Hkv + g; };
   const uint8_t* kp = a.k + tile0 * a.k_tile;
   const uint8_t* vp = a.v + tile0 * a.v_tile;
   const uint8_t* ksp = a.ks ? a.ks + tile0 * a.ks_tile : nullptr;
@@ -395,9 +399,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
   st.lsum = 0.f;
 
   const float c2 = a.c2;
-  // Tile c of the slice lies at kp + c * k_tile (and likewise for V and the
-  // scales).  Loads go through byte cursors that hold wave-uniform offsets,
-  // so addresses are a scalar base plus the lane's 16-byte offset.
+  // Tile c of a dense slice lies at kp + c * k_tile (and likewise for V and
+  // the scales).  Loads go through byte cursors that hold wave-uniform
+  // offsets, so addresses are a scalar base plus the lane's 16-byte offset.
   auto load_at = [&](Frag<FMT>& f, int64_t ok, int64_t ov, int64_t oks, int64_t ovs) {
     if constexpr (FMT == 0)
       f.load(kp + ok, vp + ov, nullptr, nullptr, lane, 0);
@@ -424,13 +428,27 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
     int64_t oks = (int64_t)first * a.ks_tile, ovs = (int64_t)first * a.vs_tile;
     const int64_t dk = (int64_t)kWaves * a.k_tile, dv = (int64_t)kWaves * a.v_tile;
     const int64_t dks = (int64_t)kWaves * a.ks_tile, dvs = (int64_t)kWaves * a.vs_tile;
+    // pool: the tile of the next load, looked up one load ahead (a scalar
+    // load whose latency the tile in between covers); lookups stop at the
+    // wave's last chunk, so only entries of the slice's rows are read
+    int cn = first;
+    const int clast = c1f - 1;
+    int64_t tn = PAGED ? pool_tile(first) : 0;
     auto load_next = [&](Frag<FMT>& f, bool advance) {
-      load_at(f, ok, ov, oks, ovs);
-      if (advance) {
-        ok += dk;
-        ov += dv;
-        oks += dks;
-        ovs += dvs;
+      if constexpr (PAGED) {
+        load_at(f, tn * a.k_tile, tn * a.v_tile, tn * a.ks_tile, tn * a.vs_tile);
+        if (advance) {
+          cn += kWaves;
+          tn = pool_tile(min(cn, clast));
+        }
+      } else {
+        load_at(f, ok, ov, oks, ovs);
+        if (advance) {
+          ok += dk;
+          ov += dv;
+          oks += dks;
+          ovs += dvs;
+        }
       }
     };
     Frag<FMT> f[NBUF];
@@ -460,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
       if (i + NBUF + k < nmine) chunk_step<FMT, false>(f[k], st, qf, c2, h, kChunk);
   }
   if (has_tail && wave == (c1 - 1 - c0) % kWaves) {
-    const int64_t c = c1 - 1;
+    const int64_t c = PAGED ? pool_tile(c1 - 1) : c1 - 1;
     Frag<FMT> t;
     load_at(t, c * a.k_tile, c * a.v_tile, c * a.ks_tile, c * a.vs_tile);
     chunk_step<FMT, true>(t, st, qf, c2, h, tail_valid);
@@ -530,15 +548,25 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
+  const bool paged = a.table != nullptr;
   switch (dtype) {
     case HX_KV_BF16:
-      hipLaunchKernelGGL(gqa_partial_kernel<0>, dim3(nwg), dim3(kThreads), 0, st, a);
+      if (paged)
+        hipLaunchKernelGGL((gqa_partial_kernel<0, true>), dim3(nwg), dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((gqa_partial_kernel<0, false>), dim3(nwg), dim3(kThreads), 0, st, a);
       break;
     case HX_KV_FP8_E4M3:
-      hipLaunchKernelGGL(gqa_partial_kernel<1>, dim3(nwg), dim3(kThreads), 0, st, a);
+      if (paged)
+        hipLaunchKernelGGL((gqa_partial_kernel<1, true>), dim3(nwg), dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((gqa_partial_kernel<1, false>), dim3(nwg), dim3(kThreads), 0, st, a);
       break;
     default:
-      hipLaunchKernelGGL(gqa_partial_kernel<2>, dim3(nwg), dim3(kThreads), 0, st, a);
+      if (paged)
+        hipLaunchKernelGGL((gqa_partial_kernel<2, true>), dim3(nwg), dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((gqa_partial_kernel<2, false>), dim3(nwg), dim3(kThreads), 0, st, a);
       break;
   }
   return hipGetLastError();

@@ -118,6 +118,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNBuf][kTileBytes];
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   __shared__ uint32_t s_over[2][kWaves];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = PAGED ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -149,8 +150,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   const int ntok = t_end > t_begin ? (int)(t_end - t_begin) : 0;
   const int ntiles = (ntok + kTileTok - 1) / kTileTok;
 
-  const int64_t tile0 = ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
-  const uint8_t* base = a.k + tile0 * a.k_tile + t_begin * kRowBytes;   // latent rows, 1152 B each
+  // Dense cache: the slice's rows are consecutive (latent rows, 1152 B
+  // each).  Block pool: 16-row group c of the slice is the tile of head g in
+  // block trow[c] (tile_of in hx_common.h), so a 32-row tile is two tiles.
+  const int64_t tile0 = PAGED ? 0 : ((int64_t)(r * a.Btot + b) * a.Hkv + g) * a.cap_chunks;
+  const uint8_t* base = a.k + tile0 * a.k_tile + t_begin * kRowBytes;
+  const int32_t* trow = PAGED ? a.table + ((int64_t)b * a.P + r) * a.cap_chunks : nullptr;
+  const int64_t cbeg = t_begin / kChunk;   // first 16-row group of the split
 
   // ---- Q^T fragments of head 32 wave + col (B operand: step s covers
   //      columns 16 s + 8 half .. +7)
@@ -169,16 +175,42 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   //      w, w + 4, ..., w + 32; lane l moves bytes 16 l .. +15 of each.  Rows
   //      past the slice end (last tile only) are fetched from row 0 of the
   //      tile instead: finite values that the masked scores give weight 0.
+  //      Block pool: the two 16-row halves come from their own blocks
+  //      (src0, src1, looked up by prep(k) before the copy); a row past the
+  //      slice end is fetched from row 0 of its half, or of the first half
+  //      when the second holds no row of the slice (then src1 = src0).
+  const uint8_t* src0 = nullptr;   // the two halves of the next tile to copy
+  const uint8_t* src1 = nullptr;
+  auto prep = [&](int k) {
+    if constexpr (PAGED) {
+      const int valid = min(kTileTok, ntok - k * kTileTok);
+      const int64_t c = cbeg + 2 * k;
+      src0 = a.k + (clamp_block(trow[c], a.num_blocks) * a.Hkv + g) * a.k_tile;
+      src1 = valid > kChunk ? a.k + (clamp_block(trow[c + 1], a.num_blocks) * a.Hkv + g) * a.k_tile : src0;
+    }
+  };
   auto load_tile = [&](int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
-    const uint8_t* src = base + (int64_t)k * kTileBytes;
     uint8_t* dst = &s_tile[k % kNBuf][0];
+    if constexpr (PAGED) {
+      constexpr int kHalfBlocks = kChunk * kRowBytes / 1024;   // 1 KiB blocks per 16-row half
 #pragma unroll
-    for (int j = 0; j < kBlocksPerWave; ++j) {
-      const int blk = wave + kWaves * j;
-      uint32_t off = blk * 1024u + 16u * opaque_lane();   // byte of the tile this lane moves
-      if (valid < kTileTok && off / kRowBytes >= (uint32_t)valid) off %= kRowBytes;
-      dma16(off, src, lds_addr(dst + blk * 1024));
+      for (int j = 0; j < kBlocksPerWave; ++j) {
+        const int blk = wave + kWaves * j;
+        const bool upper = blk >= kHalfBlocks;
+        uint32_t off = (blk - (upper ? kHalfBlocks : 0)) * 1024u + 16u * opaque_lane();   // byte of the half
+        if (valid < kTileTok && (int)(off / kRowBytes) + (upper ? kChunk : 0) >= valid) off %= kRowBytes;
+        dma16(off, upper ? src1 : src0, lds_addr(dst + blk * 1024));
+      }
+    } else {
+      const uint8_t* src = base + (int64_t)k * kTileBytes;
+#pragma unroll
+      for (int j = 0; j < kBlocksPerWave; ++j) {
+        const int blk = wave + kWaves * j;
+        uint32_t off = blk * 1024u + 16u * opaque_lane();   // byte of the tile this lane moves
+        if (valid < kTileTok && off / kRowBytes >= (uint32_t)valid) off %= kRowBytes;
+        dma16(off, src, lds_addr(dst + blk * 1024));
+      }
     }
   };
 
@@ -283,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     const int par = k & 1;
     const bool over = __any(mseen > mref + kHeadroom);   // all lanes vote, outside the lane-0 branch
     if (lane == 0) s_over[par][wave] = over ? 1u : 0u;
+    if (CUR && k + 3 < ntiles) prep(k + 3);   // pool lookups complete in the barrier's wait
     if (k + 2 < ntiles) wait_barrier<kBlocksPerWave>();
     else wait_barrier<0>();
     if ((s_over[par][0] | s_over[par][1] | s_over[par][2] | s_over[par][3]) != 0) return true;
@@ -328,7 +361,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   for (;;) {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      if (j < ntiles) load_tile(j);
+      if (j < ntiles) {
+        prep(j);
+        load_tile(j);
+      }
     bool restart = ntiles > 0 && iteration(F{}, T{}, -1);
     for (int k = 0; !restart && k + 1 < ntiles; ++k) restart = iteration(T{}, T{}, k);
     if (!restart && ntiles > 0) restart = iteration(T{}, F{}, ntiles - 1);
@@ -377,7 +413,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
 hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_partial_kernel, dim3(nwg), dim3(kThreads), 0, st, a);
+  if (a.table)
+    hipLaunchKernelGGL(mla_partial_kernel<true>, dim3(nwg), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(mla_partial_kernel<false>, dim3(nwg), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

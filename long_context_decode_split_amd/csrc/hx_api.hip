@@ -23,6 +23,8 @@ hx_status fail(hx_status s, const char* fmt, ...) {
   return s;
 }
 
+void clear_error() { g_err[0] = 0; }
+
 hx_status check_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return HX_OK;
   return fail(HX_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -199,10 +201,33 @@ hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, in
   return HX_OK;
 }
 
-hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
-                       const void* k_scale_new, const void* v_scale_new, const int64_t* pos, const int32_t* count,
-                       int32_t n_new, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace hx {
+
+// A block pool's table and size; {nullptr, 0} for a dense cache.
+struct PoolRef {
+  const int32_t* table;
+  int32_t num_blocks;
+};
+
+static hx_status check_pool(const hx_kv_desc* desc, const hx_kv_pool* pool, PoolRef* ref) {
+  if (!desc || !pool) return fail(HX_EINVAL, "null argument");
+  if (!pool->block_table || !aligned16(pool->block_table))
+    return fail(HX_EINVAL, "block_table must be a non-null 16-byte aligned device pointer");
+  if (pool->num_blocks < 1) return fail(HX_EINVAL, "num_blocks=%d must be >= 1", pool->num_blocks);
+  if (pool->reserved != 0) return fail(HX_EINVAL, "reserved must be 0");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  if ((double)pool->num_blocks * desc->Hkv * (double)g.k_tile > 9.0e18) return fail(HX_EINVAL, "pool too large");
+  *ref = PoolRef{pool->block_table, pool->num_blocks};
+  return HX_OK;
+}
+
+static hx_status kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                           const void* v_new, const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
+                           const int32_t* count, int32_t n_new, void* stream) {
   if (!desc || !cache || !pos) return fail(HX_EINVAL, "null argument");
   Geometry g;
   hx_status s = geometry(*desc, &g);
@@ -255,6 +280,8 @@ hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const v
   a.B = d.B;
   a.Hkv = d.Hkv;
   a.cap_chunks = d.cap / kChunk;
+  a.table = pool.table;
+  a.num_blocks = pool.num_blocks;
   a.n_new = n_new;
   const uint8_t* src0[4];
   for (int p = 0; p < np; ++p) src0[p] = a.src[p];
@@ -277,15 +304,15 @@ hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const v
   return HX_OK;
 }
 
-hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
-                            const int64_t* pos, const int32_t* count, int32_t n_new, void* stream) {
-  g_err[0] = 0;
+static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                                const void* v_new, const int64_t* pos, const int32_t* count, int32_t n_new,
+                                void* stream) {
   if (!desc || !cache || !pos) return fail(HX_EINVAL, "null argument");
   Geometry g;
   hx_status s = geometry(*desc, &g);
   if (s) return s;
   const hx_kv_desc& d = *desc;
-  if (d.dtype == HX_KV_BF16) return hx_kv_append(desc, cache, k_new, v_new, nullptr, nullptr, pos, count, n_new, stream);
+  if (d.dtype == HX_KV_BF16) return kv_append(desc, cache, pool, k_new, v_new, nullptr, nullptr, pos, count, n_new, stream);
   if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
   // quantised caches are GQA caches (Dk = Dv = 128, separate V)
   if (!cache->k || !k_new || !cache->v || !v_new) return fail(HX_EINVAL, "null K/V plane or input");
@@ -314,6 +341,8 @@ hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, co
   a.B = d.B;
   a.Hkv = d.Hkv;
   a.cap_chunks = d.cap / kChunk;
+  a.table = pool.table;
+  a.num_blocks = pool.num_blocks;
   a.tile_bytes = g.k_tile;
   a.sc_tile_bytes = g.ks_tile;
   a.n_new = n_new;
@@ -339,9 +368,8 @@ hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, co
   return HX_OK;
 }
 
-hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
-                        int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
-  g_err[0] = 0;
+static hx_status kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, int32_t r, int32_t b,
+                            int32_t g, int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
   if (!desc || !cache || !k_out) return fail(HX_EINVAL, "null argument");
   Geometry geo;
   hx_status s = geometry(*desc, &geo);
@@ -372,11 +400,90 @@ hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_
   a.v_tile = geo.v_tile;
   a.ks_tile = geo.ks_tile;
   a.vs_tile = geo.vs_tile;
-  a.plane_tile0 = ((int64_t)(r * d.B + b) * d.Hkv + g) * (d.cap / kChunk);
+  a.map = TileMap{pool.table, pool.num_blocks, d.P, d.B, d.Hkv, d.cap / kChunk};
+  a.r = r;
+  a.b = b;
+  a.g = g;
   a.j0 = j0;
   a.n = n;
   return check_hip(launch_dequant(a, (hipStream_t)stream), "kv_dequant launch");
 }
+
+}  // namespace hx
+
+extern "C" {
+
+hx_status hx_kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                       const void* k_scale_new, const void* v_scale_new, const int64_t* pos, const int32_t* count,
+                       int32_t n_new, void* stream) {
+  g_err[0] = 0;
+  return kv_append(desc, cache, PoolRef{nullptr, 0}, k_new, v_new, k_scale_new, v_scale_new, pos, count, n_new, stream);
+}
+
+hx_status hx_kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                            const int64_t* pos, const int32_t* count, int32_t n_new, void* stream) {
+  g_err[0] = 0;
+  return kv_append_bf16(desc, cache, PoolRef{nullptr, 0}, k_new, v_new, pos, count, n_new, stream);
+}
+
+hx_status hx_kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, int32_t r, int32_t b, int32_t g,
+                        int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
+  g_err[0] = 0;
+  return kv_dequant(desc, cache, PoolRef{nullptr, 0}, r, b, g, j0, n, k_out, v_out, stream);
+}
+
+hx_status hx_kv_append_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new, const void* v_new,
+                             const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
+                             const int32_t* count, int32_t n_new, void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return kv_append(desc, &pool->planes, ref, k_new, v_new, k_scale_new, v_scale_new, pos, count, n_new, stream);
+}
+
+hx_status hx_kv_append_bf16_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new,
+                                  const void* v_new, const int64_t* pos, const int32_t* count, int32_t n_new,
+                                  void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return kv_append_bf16(desc, &pool->planes, ref, k_new, v_new, pos, count, n_new, stream);
+}
+
+hx_status hx_kv_dequant_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, int32_t r, int32_t b, int32_t g,
+                              int64_t j0, int64_t n, float* k_out, float* v_out, void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return kv_dequant(desc, &pool->planes, ref, r, b, g, j0, n, k_out, v_out, stream);
+}
+
+hx_status hx_pool_layout(const hx_kv_desc* desc, int32_t num_blocks, hx_kv_layout_info* out) {
+  g_err[0] = 0;
+  if (!desc || !out) return fail(HX_EINVAL, "null argument");
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  if (num_blocks < 1) return fail(HX_EINVAL, "num_blocks=%d must be >= 1", num_blocks);
+  const double tiles = (double)num_blocks * desc->Hkv;
+  if (tiles * (double)g.k_tile > 9.0e18) return fail(HX_EINVAL, "pool too large");
+  const int64_t t = (int64_t)num_blocks * desc->Hkv;
+  out->k_tile_bytes = (size_t)g.k_tile;
+  out->v_tile_bytes = (size_t)g.v_tile;
+  out->k_bytes = (size_t)(t * g.k_tile);
+  out->v_bytes = (size_t)(t * g.v_tile);
+  out->k_scale_bytes = (size_t)(t * g.ks_tile);
+  out->v_scale_bytes = (size_t)(t * g.vs_tile);
+  out->n_max = (int64_t)desc->P * desc->cap;
+  return HX_OK;
+}
+
+}  // extern "C"
+
+namespace hx {
 
 static hx_status check_heads(const hx_kv_desc& d, const Geometry& geo, int32_t Hq) {
   if (Hq < 1 || Hq % d.Hkv) return fail(HX_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", Hq, d.Hkv);
@@ -385,6 +492,10 @@ static hx_status check_heads(const hx_kv_desc& d, const Geometry& geo, int32_t H
   if (geo.kind == 1 && G != 128) return fail(HX_EUNSUPPORTED, "MLA kernel takes 128 query heads per latent head (G=%d)", G);
   return HX_OK;
 }
+
+}  // namespace hx
+
+extern "C" {
 
 hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes) {
   g_err[0] = 0;
@@ -404,13 +515,16 @@ hx_status hx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return check_hip(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream), "workspace memset");
 }
 
+}  // extern "C"
+
+namespace hx {
+
 // The partial pass of a decode step.  With o_final / lse_final (hx_decode_attn)
 // the slice partials go to workspace scratch and one more kernel folds every
 // slice's partial or split records straight into the final output.
-static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
-                             const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
-                             size_t ws_bytes, void* stream, float* o_final, float* lse_final) {
-  g_err[0] = 0;
+static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* q,
+                             int32_t Hq, const int64_t* ctx_len, float scale, float* o_part, float* lse_part,
+                             void* ws, size_t ws_bytes, void* stream, float* o_final, float* lse_final) {
   const bool final_out = o_final != nullptr;
   if (!desc || !cache || !q || !ctx_len || !ws) return fail(HX_EINVAL, "null argument");
   if (final_out ? !lse_final : (!o_part || !lse_part)) return fail(HX_EINVAL, "null argument");
@@ -459,6 +573,8 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, c
   a.Dk = d.Dk;
   a.Dv = d.Dv;
   a.cap_chunks = d.cap / kChunk;
+  a.table = pool.table;
+  a.num_blocks = pool.num_blocks;
   a.k_tile = geo.k_tile;
   a.v_tile = d.v_alias_k ? geo.k_tile : geo.v_tile;
   a.ks_tile = geo.ks_tile;
@@ -510,20 +626,47 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, c
   return HX_OK;
 }
 
+}  // namespace hx
+
+extern "C" {
+
 hx_status hx_decode_attn_partial(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
                                  const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
                                  size_t ws_bytes, void* stream) {
-  return decode_step(desc, cache, q, Hq, ctx_len, scale, o_part, lse_part, ws, ws_bytes, stream, nullptr, nullptr);
+  g_err[0] = 0;
+  return decode_step(desc, cache, PoolRef{nullptr, 0}, q, Hq, ctx_len, scale, o_part, lse_part, ws, ws_bytes, stream,
+                     nullptr, nullptr);
 }
 
 hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
                          const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream) {
-  if (!o) {
-    g_err[0] = 0;
-    return fail(HX_EINVAL, "null argument");
-  }
-  return decode_step(desc, cache, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
+  g_err[0] = 0;
+  if (!o) return fail(HX_EINVAL, "null argument");
+  return decode_step(desc, cache, PoolRef{nullptr, 0}, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream,
+                     o, lse);
+}
+
+hx_status hx_decode_attn_partial_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,
+                                       const int64_t* ctx_len, float scale, float* o_part, float* lse_part, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return decode_step(desc, &pool->planes, ref, q, Hq, ctx_len, scale, o_part, lse_part, ws, ws_bytes, stream, nullptr,
+                     nullptr);
+}
+
+hx_status hx_decode_attn_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,
+                               const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                               void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  if (!o) return fail(HX_EINVAL, "null argument");
+  return decode_step(desc, &pool->planes, ref, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
 }
 
 hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,

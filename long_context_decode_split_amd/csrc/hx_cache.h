@@ -18,6 +18,8 @@ struct AppendArgs {
   int nplanes;
   int P, B, Hkv;
   int64_t cap_chunks;
+  const int32_t* table;    // pool cache block table (null: dense)
+  int32_t num_blocks;
   int n_new;
   int max_chunks;          // largest number of chunks one request touches
   int64_t pos[kMaxBatchPerLaunch];
@@ -36,6 +38,8 @@ struct QAppendArgs {
   int D;
   int P, B, Hkv;
   int64_t cap_chunks;
+  const int32_t* table;    // pool cache block table (null: dense)
+  int32_t num_blocks;
   int64_t tile_bytes;      // code bytes per chunk tile
   int64_t sc_tile_bytes;   // scale bytes per chunk tile
   int n_new;
@@ -55,7 +59,8 @@ struct DequantArgs {
   float* v_out;
   int dtype, lay_k, lay_v, Dk, Dv, v_alias;
   int64_t k_tile, v_tile, ks_tile, vs_tile;
-  int64_t plane_tile0;     // tile index of (r, b, g, chunk 0)
+  TileMap map;             // tile addressing of the cache
+  int r, b, g;             // the slice rows read: slice r of request b, KV head g
   int64_t j0, n;
 };
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);

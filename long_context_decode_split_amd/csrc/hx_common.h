@@ -157,6 +157,29 @@ HXHD void tile_inv(int lay, int width, int64_t off2, int* m, int* d) {
   }
 }
 
+// ---------------------------------------------------------------- tile addressing
+// Dense cache: tile (slice r, request b, KV head g, local 16-row group c) is
+// tile ((r * B + b) * Hkv + g) * cap_chunks + c of every plane.  Block pool:
+// group c of slice r of request b is block table[(b * P + r) * cap_chunks +
+// c]; a block holds the tiles of all Hkv heads, so the tile is
+// block * Hkv + g.  Block ids outside [0, num_blocks) are clamped into it:
+// a bad table reads wrong rows but never leaves the planes.
+struct TileMap {
+  const int32_t* table;   // device [B][P][cap_chunks]; null for a dense cache
+  int32_t num_blocks;
+  int P, B, Hkv;
+  int64_t cap_chunks;
+};
+
+HXHD int64_t clamp_block(int32_t blk, int32_t num_blocks) {
+  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+
+HXHD int64_t tile_of(const TileMap& m, int r, int b, int g, int64_t c) {
+  if (!m.table) return ((int64_t)(r * m.B + b) * m.Hkv + g) * m.cap_chunks + c;
+  return clamp_block(m.table[((int64_t)b * m.P + r) * m.cap_chunks + c], m.num_blocks) * m.Hkv + g;
+}
+
 // ---------------------------------------------------------------- cache geometry
 struct Geometry {
   int kind;            // 0 GQA (Dk = Dv = 128), 1 MLA (576 / 512, aliased, bf16)
@@ -171,8 +194,9 @@ struct Geometry {
 // combination with no kernel.
 hx_status geometry(const hx_kv_desc& d, Geometry* g);
 
-// Error reporting (thread-local message).
+// Error reporting (thread-local message; entry points clear it first).
 hx_status fail(hx_status s, const char* fmt, ...);
+void clear_error();
 hx_status check_hip(hipError_t e, const char* what);
 
 // ---------------------------------------------------------------- launchers
@@ -188,6 +212,8 @@ struct PartialArgs {
   float* ws_lse;           // [records][G]
   int P, Btot, b0, nb, Hkv, Hq, G, Dk, Dv;
   int64_t cap_chunks;
+  const int32_t* table;    // block table of a pool cache (tile addressing above); null: dense
+  int32_t num_blocks;
   int64_t k_tile, v_tile, ks_tile, vs_tile;
   float c2;                // softmax scale * log2(e)
   int cpw;                 // chunks per workgroup (split size)
@@ -196,6 +222,8 @@ struct PartialArgs {
   int wg_begin[kMaxBatchPerLaunch + 1];     // first workgroup (= split record) of each request
   int fold_begin[kMaxBatchPerLaunch + 1];   // first fold workgroup of each request
 };
+HXHD TileMap tile_map(const PartialArgs& a) { return TileMap{a.table, a.num_blocks, a.P, a.Btot, a.Hkv, a.cap_chunks}; }
+
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
 hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
 // Folds the split records of every slice with more than one split into the

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   if (end == pos || row0 >= end) return;   // nothing of this request lands in this chunk
   const int r = (int)(c % a.P);
   const int64_t lc = c / a.P;
-  const int64_t tile = ((int64_t)(r * a.B + b) * a.Hkv + g) * a.cap_chunks + lc;
+  const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, lc);
   const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new;   // token-major source, this launch's rows
   const uint8_t* src = a.src[plane];
   uint8_t* dst = a.dst[plane] + tile * a.tile_bytes[plane];
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a, int64
     if (!a.v_out) return;
   }
   const int64_t j = a.j0 + i;
-  const int64_t tile = a.plane_tile0 + j / kChunk;
+  const int64_t tile = tile_of(a.map, a.r, a.b, a.g, j / kChunk);
   const int mm = (int)(j % kChunk);
   const bool from_k = !is_v || a.v_alias;
   const uint8_t* plane = from_k ? a.k : a.v;

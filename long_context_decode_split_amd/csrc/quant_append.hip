@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(const QAppendArg
   const int m_lo = (int)(pos > row0 ? pos - row0 : 0);   // rows below m_lo were stored earlier
   const int m_hi = (int)(end - row0 < kChunk ? end - row0 : kChunk);
   const int r = (int)(c % a.P);
-  const int64_t tile = ((int64_t)(r * a.B + b) * a.Hkv + g) * a.cap_chunks + c / a.P;
+  const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, c / a.P);
   const int D = a.D;
   const int lay = a.lay[plane];
   // new row m of this tile is source token (row0 + m - pos) of this (request, head)
