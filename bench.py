@@ -29,13 +29,37 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def setup(w, seed, append_bf16=False):
+def make_pool(desc, inp, seed):
+    """A block pool holding every request's n tokens: lists grown by the host
+    allocator, then each request's blocks shuffled among themselves (seeded)
+    so that consecutive 16-row groups of a slice sit at scattered places of
+    the pool, as after a long run of interleaved growth and recycling."""
+    need = 0
+    for n in inp.ctx:
+        for r in range(desc.P):
+            need += -(-api.slice_len(n, desc.P, r) // 16)
+    pool = api.KVPool(desc, need, device="cuda")
+    rng = np.random.default_rng(seed + 7)
+    for b, n in enumerate(inp.ctx):
+        pool.reserve(b, n)
+        ids = pool.table_host[b][pool.table_host[b] >= 0]
+        pool.table_host[b][pool.table_host[b] >= 0] = rng.permutation(ids)
+    pool.sync()
+    return pool
+
+
+def setup(w, seed, append_bf16=False, layout="dense"):
     t0 = time.time()
     inp = synth.make_inputs(w, seed, device="cuda")
     desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=w.v_alias_k, dtype=w.dtype, cap=inp.cap)
-    cache = api.KVCache(desc, device="cuda")
+    if layout == "paged":
+        cache = make_pool(desc, inp, seed)
+        append = api.kv_append_paged
+    else:
+        cache = api.KVCache(desc, device="cuda")
+        append = api.kv_append
     # the cache holds n-1 tokens of every request before the step
-    api.kv_append(cache, inp.k, inp.v, inp.k_scale, inp.v_scale, pos=[0] * w.B, count=[n - 1 for n in inp.ctx])
+    append(cache, inp.k, inp.v, inp.k_scale, inp.v_scale, pos=[0] * w.B, count=[n - 1 for n in inp.ctx])
     last = [n - 1 for n in inp.ctx]
 
     def newest(t):
@@ -61,6 +85,10 @@ def setup(w, seed, append_bf16=False):
     return inp, cache, step_in, ws, o_part, lse_part, o, lse
 
 
+def traffic_key(w, layout):
+    return w.name if layout == "dense" else f"{w.name}+{layout}"
+
+
 def kernel_src_hash(w):
     """Hash of the partial kernel's sources for workload w, to tell whether
     recorded counters still describe the kernel that runs."""
@@ -73,15 +101,15 @@ def kernel_src_hash(w):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(w):
+def recorded_traffic(w, layout="dense"):
     """HBM bytes per launch of the partial kernel from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json (scaled by
     a copy of known size), or None when none was recorded for this workload
-    or the kernel sources changed since."""
+    and cache layout, or the kernel sources changed since."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(w.name)
+            rec = json.load(f).get(traffic_key(w, layout))
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_src_sha16") != kernel_src_hash(w):
@@ -153,6 +181,9 @@ def main():
     ap.add_argument("--attn", choices=("partial+combine", "one-call"), default="partial+combine",
                     help="partial+combine: hx_decode_attn_partial then hx_lse_combine (the slice partials are "
                          "outputs); one-call: hx_decode_attn (final O and LSE only; one launch for small problems)")
+    ap.add_argument("--layout", choices=("dense", "paged"), default="dense",
+                    help="dense: [P][B][Hkv][cap/16] cache planes; paged: a block pool with per-(request, slice) "
+                         "16-row block lists, each request's blocks shuffled among themselves (the *_paged calls)")
     ap.add_argument("--flush-cache", action="store_true",
                     help="write a 1 GiB buffer before every step (outside the timed events) so that no KV bytes "
                          "survive in L2 or the 256 MB MALL; steps are then timed one by one")
@@ -179,22 +210,28 @@ def main():
         sys.exit(2)
 
     w = configs.ALL[args.workload]
-    inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed, append_bf16=args.append == "bf16")
+    inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed, append_bf16=args.append == "bf16",
+                                                         layout=args.layout)
     stream = torch.cuda.current_stream()
+    paged = args.layout == "paged"
+    append_bf16 = api.kv_append_bf16_paged if paged else api.kv_append_bf16
+    append_codes = api.kv_append_paged if paged else api.kv_append
+    attn_one = api.decode_attn_paged if paged else api.decode_attn
+    attn_partial = api.decode_attn_partial_paged if paged else api.decode_attn_partial
 
     def step(ev=None):
         if args.append == "bf16":
-            api.kv_append_bf16(cache, st["kb"], st["vb"], pos=st["pos"], stream=stream)
+            append_bf16(cache, st["kb"], st["vb"], pos=st["pos"], stream=stream)
         else:
-            api.kv_append(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
+            append_codes(cache, st["k"], st["v"], st["ks"], st["vs"], pos=st["pos"], stream=stream)
         if ev is not None:
             ev[0].record(stream)
         if args.attn == "one-call":
-            api.decode_attn(cache, inp.q, inp.ctx, w.softmax_scale, o, lse, ws, stream=stream)
+            attn_one(cache, inp.q, inp.ctx, w.softmax_scale, o, lse, ws, stream=stream)
             if ev is not None:
                 ev[1].record(stream)
             return
-        api.decode_attn_partial(cache, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws, stream=stream)
+        attn_partial(cache, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         api.lse_combine(o_part, lse_part, o, lse, stream=stream)
@@ -260,15 +297,16 @@ def main():
             "context": inp.ctx if w.ctx is None else w.ctx, "kv_bytes_per_step": nbytes, "seed": args.seed,
             "append": "bf16 values quantised on the device" if args.append == "bf16" else "storage format",
             "attention": args.attn,
+            "layout": "block pool, 16-row blocks shuffled within each request" if paged else "dense planes",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_attn" if args.attn == "one-call" else "decode_attn_partial",
+            "kernel": ("decode_attn" if args.attn == "one-call" else "decode_attn_partial") + ("_paged" if paged else ""),
             "achieved": round(kern_gbs, 2),
             "peak": peak_gbs,
             "unit": "GB/s",
             "frac": round(kern_gbs / peak_gbs, 4),
-            "traffic": recorded_traffic(w),
+            "traffic": recorded_traffic(w, args.layout),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
         },
