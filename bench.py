@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--layout", choices=("dense", "paged"), default="dense",
                     help="dense: [P][B][Hkv][cap/16] cache planes; paged: a block pool with per-(request, slice) "
                          "16-row block lists, each request's blocks shuffled among themselves (the *_paged calls)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one captured HIP graph per step (the partial call is still timed on "
+                         "eager launches)")
     ap.add_argument("--flush-cache", action="store_true",
                     help="write a 1 GiB buffer before every step (outside the timed events) so that no KV bytes "
                          "survive in L2 or the 256 MB MALL; steps are then timed one by one")
@@ -219,7 +222,7 @@ def main():
     attn_one = api.decode_attn_paged if paged else api.decode_attn
     attn_partial = api.decode_attn_partial_paged if paged else api.decode_attn_partial
 
-    def step(ev=None):
+    def step(ev=None, stream=stream):
         if args.append == "bf16":
             append_bf16(cache, st["kb"], st["vb"], pos=st["pos"], stream=stream)
         else:
@@ -260,6 +263,32 @@ def main():
     kern_avg_ms = float(np.mean(kern_ms))
     # back-to-back steps: total over the timed region; flushed steps: each step on its own
     step_ms = float(np.mean(step_each_ms)) if flush is not None else start.elapsed_time(end) / args.steps
+    if args.graph:
+        # the same step captured once and replayed: no host launch work between its kernels
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [(new_ev(), new_ev()) for _ in range(args.steps)]
+        start.record(stream)
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(i & 0xFF)
+            gev[i][0].record(stream)
+            graph.replay()
+            gev[i][1].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        step_each_ms = [a.elapsed_time(b) for a, b in gev]
+        step_ms = float(np.mean(step_each_ms)) if flush is not None else start.elapsed_time(end) / args.steps
     pct = lambda x: {f"p{q}": round(float(np.percentile(x, q)) * 1e3, 2) for q in (10, 50, 90)}
 
     nbytes = roofline.kv_bytes(w, inp.ctx)
@@ -298,6 +327,7 @@ def main():
             "append": "bf16 values quantised on the device" if args.append == "bf16" else "storage format",
             "attention": args.attn,
             "layout": "block pool, 16-row blocks shuffled within each request" if paged else "dense planes",
+            "launch": "one HIP graph replay per step" if args.graph else "eager launches",
         },
         "roofline": {
             "bound": "hbm",

@@ -80,6 +80,9 @@ __device__ __forceinline__ s16x4 as_s16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(s16x4, t);
 }
 
+__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
 // Two fp32 -> packed bf16 pair, round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -277,17 +280,28 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
 
   // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
   if constexpr (FMT == 0) {
+    // P enters the matrix cores as two bf16 fragments, its rounding and the
+    // bf16 of the residual, so the products carry about 16 significant bits
+    // of P: with one bf16 fragment the output error can reach 2^-8 times half
+    // the range of V (a few weights dominate in short slices), above the
+    // 2e-3 bound for bf16 caches.  The second set of products is cheap here:
+    // bf16 tiles leave the matrix cores mostly idle.
     const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-    st.lsum_mfma = add_bf16x2(p23, add_bf16x2(p01, st.lsum_mfma));
-    const s16x4 pb = as_s16x4(p01, p23);
+    const uint32_t r01 = pack_bf16(p[0] - bf16lo(p01), p[1] - bf16hi(p01));
+    const uint32_t r23 = pack_bf16(p[2] - bf16lo(p23), p[3] - bf16hi(p23));
+    st.lsum_mfma = add_bf16x2(r23, add_bf16x2(r01, add_bf16x2(p23, add_bf16x2(p01, st.lsum_mfma))));
+    const s16x4 ph = as_s16x4(p01, p23), pl = as_s16x4(r01, r23);
+    s16x4 va[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 vv = cur.v[i];
-      st.acc[2 * i] =
-          __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.x & keep01, vv.y & keep23), pb, st.acc[2 * i], 0, 0, 0);
-      st.acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vv.z & keep01, vv.w & keep23), pb,
-                                                                     st.acc[2 * i + 1], 0, 0, 0);
+      va[2 * i] = as_s16x4(vv.x & keep01, vv.y & keep23);
+      va[2 * i + 1] = as_s16x4(vv.z & keep01, vv.w & keep23);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[i], ph, st.acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[i], pl, st.acc[i], 0, 0, 0);
   } else if constexpr (FMT == 1) {
     // The tile's V scale is folded into P; the rounded products, divided by
     // the scale, are what normalises O.

@@ -377,6 +377,38 @@ def test_decode_attn_whole_step(w):
     H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
 
 
+EDGE_CASES = [
+    configs.TINY_GQA.scaled(B=70, Hkv=1, Hq=3, ctx=None, ctx_range=(1, 200), P=3),        # B > 64: two launches, G=3
+    configs.TINY_GQA.scaled(B=2, Hkv=8, Hq=8, ctx=None, ctx_range=(1, 3000), P=64),       # P = 64, G = 1, 8 KV heads
+    configs.FP8_GQA.scaled(B=66, Hkv=2, Hq=10, ctx=None, ctx_range=(1, 300), P=2),       # fp8, G = 5, two launches
+    configs.MXFP4_RAGGED.scaled(B=65, Hkv=1, Hq=7, ctx_range=(1, 500), P=5),              # MXFP4, G = 7, two launches
+    configs.LLAMA405B_SHARE.scaled(B=2, Hkv=2, Hq=32, ctx=None, ctx_range=(3000, 30000)),   # G = 16 with 2 KV heads
+    configs.DEEPSEEK_MLA.scaled(B=66, ctx=None, ctx_range=(1, 100), P=1),                 # MLA, P = 1, two launches
+]
+
+
+@pytest.mark.parametrize("w", EDGE_CASES, ids=_ids)
+def test_edge_shapes(w):
+    """Batches that take several launches, the largest slice count, odd and
+    unit group widths, several KV heads of 16 query heads each, MLA with one
+    slice: partials, combine and the one-call step against the oracle."""
+    seed = 5 + len(_ids(w))
+    H.log(f"[edge] {_ids(w)} seed={seed}")
+    inp = synth.make_inputs(w, seed, device=DEV, needles=True)
+    cache = H.build_cache(inp)
+    o_part, lse_part, ws = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    o1 = torch.full_like(o, float("nan"))
+    l1 = torch.full_like(lse, float("nan"))
+    api.decode_attn(cache, inp.q, inp.ctx, w.softmax_scale, o1, l1, ws)
+    torch.cuda.synchronize()
+    heads = [0, 31, 64, 127] if w.Hq == 128 else None
+    groups = H.all_groups(inp) if w.B * w.Hkv <= 16 else [(b, g) for b in (0, 1, 63, 64, w.B - 1) for g in range(w.Hkv)]
+    worst = H.check_step(inp, o_part, lse_part, o, lse, groups=groups, heads=heads, label=_ids(w))
+    H.check_step(inp, o_part, lse_part, o1, l1, groups=groups, heads=heads, label=_ids(w) + " one-call")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
 @pytest.mark.parametrize("P", [1, 3, 8, 100])
 def test_lse_combine_matches_oracle(P):
     g = torch.Generator(device="cpu").manual_seed(P)
