@@ -48,10 +48,11 @@ def make_pool(desc, inp, seed):
     return pool
 
 
-def setup(w, seed, append_bf16=False, layout="dense"):
+def setup(w, seed, append_bf16=False, layout="dense", flags=0):
     t0 = time.time()
     inp = synth.make_inputs(w, seed, device="cuda")
-    desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=w.v_alias_k, dtype=w.dtype, cap=inp.cap)
+    desc = api.KVDesc(P=w.P, B=w.B, Hkv=w.Hkv, Dk=w.Dk, Dv=w.Dv, v_alias_k=w.v_alias_k, dtype=w.dtype, cap=inp.cap,
+                      flags=flags)
     if layout == "paged":
         cache = make_pool(desc, inp, seed)
         append = api.kv_append_paged
@@ -184,6 +185,8 @@ def main():
     ap.add_argument("--layout", choices=("dense", "paged"), default="dense",
                     help="dense: [P][B][Hkv][cap/16] cache planes; paged: a block pool with per-(request, slice) "
                          "16-row block lists, each request's blocks shuffled among themselves (the *_paged calls)")
+    ap.add_argument("--p-bf16", action="store_true",
+                    help="HX_FLAG_P_BF16: the MLA value product takes P rounded once to bf16 (faster, less precise)")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one captured HIP graph per step (the partial call is still timed on "
                          "eager launches)")
@@ -214,7 +217,8 @@ def main():
 
     w = configs.ALL[args.workload]
     inp, cache, st, ws, o_part, lse_part, o, lse = setup(w, args.seed, append_bf16=args.append == "bf16",
-                                                         layout=args.layout)
+                                                         layout=args.layout,
+                                                         flags=api.HX_FLAG_P_BF16 if args.p_bf16 else 0)
     stream = torch.cuda.current_stream()
     paged = args.layout == "paged"
     append_bf16 = api.kv_append_bf16_paged if paged else api.kv_append_bf16
@@ -328,6 +332,8 @@ def main():
             "attention": args.attn,
             "layout": "block pool, 16-row blocks shuffled within each request" if paged else "dense planes",
             "launch": "one HIP graph replay per step" if args.graph else "eager launches",
+            "p_in_value_product": ("bf16, rounded once" if args.p_bf16 or w.dtype != "bf16"
+                                   else "bf16 high part + bf16 residual"),
         },
         "roofline": {
             "bound": "hbm",

@@ -9,13 +9,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhelixdec
 
 HX_OK, HX_EINVAL, HX_EUNSUPPORTED, HX_EHIP, HX_ENOSPC = 0, 1, 2, 3, 4
 HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4 = 0, 1, 2
+HX_FLAG_P_BF16 = 1
 STATUS_NAMES = {0: "HX_OK", 1: "HX_EINVAL", 2: "HX_EUNSUPPORTED", 3: "HX_EHIP", 4: "HX_ENOSPC"}
 
 
 class hx_kv_desc(ctypes.Structure):
     _fields_ = [("P", ctypes.c_int32), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Dk", ctypes.c_int32),
                 ("Dv", ctypes.c_int32), ("v_alias_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("cap", ctypes.c_int64)]
+                ("flags", ctypes.c_int32), ("cap", ctypes.c_int64)]
 
 
 class hx_kv_cache(ctypes.Structure):

@@ -12,10 +12,10 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from ._lib import (HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXError, check, hx_kv_cache, hx_kv_desc,
-                   hx_kv_layout_info, hx_kv_pool, lib)
+from ._lib import (HX_FLAG_P_BF16, HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXError, check, hx_kv_cache,
+                   hx_kv_desc, hx_kv_layout_info, hx_kv_pool, lib)
 
-__all__ = ["HXError", "KVDesc", "KVCache", "KVPool", "DTYPES", "kv_layout", "pool_layout", "slot", "slice_len",
+__all__ = ["HXError", "HX_FLAG_P_BF16", "KVDesc", "KVCache", "KVPool", "DTYPES", "kv_layout", "pool_layout", "slot", "slice_len",
            "kv_tile_offset", "kv_append", "kv_append_bf16", "kv_dequant", "kv_append_paged", "kv_append_bf16_paged",
            "kv_dequant_paged", "workspace_size", "workspace_init", "decode_attn_partial", "decode_attn",
            "decode_attn_partial_paged", "decode_attn_paged", "lse_combine", "version", "exported_symbols"]
@@ -34,10 +34,11 @@ class KVDesc:
     v_alias_k: bool
     dtype: str
     cap: int
+    flags: int = 0      # HX_FLAG_P_BF16: MLA value product with P rounded once to bf16
 
     def c(self):
-        return hx_kv_desc(self.P, self.B, self.Hkv, self.Dk, self.Dv, int(self.v_alias_k), DTYPES[self.dtype], 0,
-                          self.cap)
+        return hx_kv_desc(self.P, self.B, self.Hkv, self.Dk, self.Dv, int(self.v_alias_k), DTYPES[self.dtype],
+                          int(self.flags), self.cap)
 
 
 def _stream(stream):

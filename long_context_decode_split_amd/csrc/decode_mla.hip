@@ -16,6 +16,11 @@
 // sums are exchanged and every score is computed once.  The softmax keeps
 // the first tile's max as its reference, so the accumulator never needs
 // rescaling (a score more than 2^kHeadroom above it restarts the run).
+// P enters the value product as a bf16 high part plus the bf16 of its
+// rounding residual (SPLITP, the default): rounded once, P's 8 significant
+// bits put the output's error at up to 2^-8 times half the range of V, which
+// for short slices reaches the 2e-3 bound of bf16 caches; the residual's
+// products double the value product's matrix-core work (measured +27%).
 //
 // A tile (two chunk tiles, 36 KiB) is copied from HBM into LDS unchanged with
 // direct global-to-LDS loads (no VGPRs), into one of four buffers: three
@@ -118,7 +123,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-template <bool PAGED>
+template <bool PAGED, bool SPLITP>
 __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNBuf][kTileBytes];
@@ -271,6 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   //      unchanged: O and the sums share the reference, and
   //      LSE = mref + log2(sum).  P goes out as bf16 pairs in pk.
   uint32_t pk[8];
+  uint32_t pr[8];   // SPLITP: bf16 of the rounding residuals of P, same layout
   float mseen = -INFINITY;   // largest scaled score seen in this run (base 2)
   auto softmax = [&](f32x16 sc, int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
@@ -294,6 +300,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       pk[i] = __builtin_bit_cast(uint32_t, pb2);
       // the rounded values the matrix product uses, summed for the normalisation
       lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, lsum_mfma, false);
+      if constexpr (SPLITP) {
+        const float r0 = p0 - __uint_as_float(pk[i] << 16), r1 = p1 - __uint_as_float(pk[i] & 0xffff0000u);
+        const bf16x2 rb2 = {(__bf16)r0, (__bf16)r1};
+        pr[i] = __builtin_bit_cast(uint32_t, rb2);
+        lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(rb2, kOnes2, lsum_mfma, false);
+      }
     }
   };
 
@@ -342,6 +354,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
             __builtin_bit_cast(bf16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
         acc[s & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[s % 3]), pb, acc[s & 15],
                                                               0, 0, 0);
+        if constexpr (SPLITP) {   // the residual's products, on the same value fragment
+          const bf16x8 pl =
+              __builtin_bit_cast(bf16x8, make_uint4(pr[4 * u], pr[4 * u + 1], pr[4 * u + 2], pr[4 * u + 3]));
+          acc[s & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[s % 3]), pl,
+                                                                acc[s & 15], 0, 0, 0);
+        }
       }
       if (NEXT) {
         if (s + kKPre < kSteps) kv[(s + kKPre) % (kKPre + 1)] = kread(tk, s + kKPre);
@@ -413,10 +431,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
 hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
-  if (a.table)
-    hipLaunchKernelGGL(mla_partial_kernel<true>, dim3(nwg), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(mla_partial_kernel<false>, dim3(nwg), dim3(kThreads), 0, st, a);
+  const dim3 grid(nwg), block(kThreads);
+  if (a.table) {
+    if (a.split_p)
+      hipLaunchKernelGGL((mla_partial_kernel<true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((mla_partial_kernel<true, false>), grid, block, 0, st, a);
+  } else {
+    if (a.split_p)
+      hipLaunchKernelGGL((mla_partial_kernel<false, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((mla_partial_kernel<false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ hx_status geometry(const hx_kv_desc& d, Geometry* g) {
   if (d.B < 1) return fail(HX_EINVAL, "B=%d must be >= 1", d.B);
   if (d.Hkv < 1) return fail(HX_EINVAL, "Hkv=%d must be >= 1", d.Hkv);
   if (d.cap < kChunk || d.cap % kChunk) return fail(HX_EINVAL, "cap=%lld must be a positive multiple of 16", (long long)d.cap);
-  if (d.reserved != 0) return fail(HX_EINVAL, "reserved must be 0");
+  if (d.flags & ~HX_FLAG_P_BF16) return fail(HX_EINVAL, "unknown flags 0x%x", d.flags);
   if (d.dtype < HX_KV_BF16 || d.dtype > HX_KV_MXFP4) return fail(HX_EINVAL, "unknown dtype %d", d.dtype);
   if (d.v_alias_k != 0 && d.v_alias_k != 1) return fail(HX_EINVAL, "v_alias_k must be 0 or 1");
   if (d.Dk < 1 || d.Dv < 1) return fail(HX_EINVAL, "Dk and Dv must be positive");
@@ -580,6 +580,7 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   a.ks_tile = geo.ks_tile;
   a.vs_tile = d.v_alias_k ? geo.ks_tile : geo.vs_tile;
   a.c2 = scale * 1.44269504088896341f;
+  a.split_p = (d.flags & HX_FLAG_P_BF16) == 0;
   const int64_t records = ws_records(d, geo.kind);
   const int target = target_wgs(geo.kind, d.dtype);
   const int minc = min_chunks_per_wg(geo.kind);

@@ -216,6 +216,7 @@ struct PartialArgs {
   int32_t num_blocks;
   int64_t k_tile, v_tile, ks_tile, vs_tile;
   float c2;                // softmax scale * log2(e)
+  int split_p;             // MLA: P as bf16 high part + residual (else rounded once)
   int cpw;                 // chunks per workgroup (split size)
   int64_t n[kMaxBatchPerLaunch];
   int nsplit[kMaxBatchPerLaunch];

@@ -136,6 +136,7 @@ def test_tile_offset_errors():
 @pytest.mark.parametrize("bad,status", [
     (dict(P=0), _lib.HX_EINVAL), (dict(P=65), _lib.HX_EINVAL), (dict(cap=40), _lib.HX_EINVAL),
     (dict(cap=0), _lib.HX_EINVAL), (dict(B=0), _lib.HX_EINVAL), (dict(Dk=64, Dv=64), _lib.HX_EUNSUPPORTED),
+    (dict(flags=2), _lib.HX_EINVAL), (dict(flags=-1), _lib.HX_EINVAL),
     (dict(Dk=576, Dv=512, v_alias_k=False), _lib.HX_EUNSUPPORTED),
     (dict(Dk=576, Dv=512, v_alias_k=True, dtype="fp8_e4m3"), _lib.HX_EUNSUPPORTED),
 ])

@@ -6,6 +6,8 @@ Bars: placement and dequantisation bit-exact; O within 2e-3 (bf16 KV) or
 2e-2 (fp8 / MXFP4 KV, oracle on the dequantised values) absolute and 1e-2 /
 5e-2 relative to max |O|; LSE within 1e-4 relative (helpers.TOL)."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -297,6 +299,26 @@ def test_gqa_score_jumps(dtype, staircase):
     torch.cuda.synchronize()
     worst = H.check_step(inp, o_part, lse_part, o, lse, label=f"gqa jumps {dtype} staircase={staircase}")
     H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
+def test_mla_value_product_precision():
+    """Short slices, where a few weights dominate: with P split into a bf16
+    high part and residual (default) the MLA output is within ~1e-5 of the
+    oracle over all 128 heads; with HX_FLAG_P_BF16 (P rounded once) the
+    error is of the order 2^-8 times V's spread, still within 2e-3 here."""
+    w = configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(1, 40), P=8)
+    inp = synth.make_inputs(w, 40, device=DEV)
+    worst = {}
+    for flags in (0, api.HX_FLAG_P_BF16):
+        desc = dataclasses.replace(H.desc_of(inp), flags=flags)
+        cache = api.KVCache(desc, device=DEV, fill=0xFF)
+        api.kv_append(cache, inp.k, None, None, None, pos=[0] * w.B, count=inp.ctx)
+        o_part, lse_part, _ = H.run_partials(inp, cache)
+        o, lse = H.run_combine(o_part, lse_part)
+        torch.cuda.synchronize()
+        worst[flags] = H.check_step(inp, o_part, lse_part, o, lse, label=f"mla flags={flags}")[0]
+    H.log(f"   worst |dO| split P {worst[0]:.2e}, P rounded once {worst[1]:.2e}")
+    assert worst[0] <= 2e-5 < worst[1]
 
 
 def test_partials_are_deterministic_and_workspace_reusable():
