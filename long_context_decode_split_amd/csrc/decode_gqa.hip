@@ -37,7 +37,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
-constexpr int kWaves = kGqaWavesPerWg;
 
 // Chunk tiles a wave keeps in flight (register budget: 32 VGPRs per bf16 tile).
 #ifndef HX_GQA_TILES_BF16
@@ -51,7 +50,6 @@ constexpr int kWaves = kGqaWavesPerWg;
 #endif
 template <int FMT>
 constexpr int kTilesInFlight = FMT == 0 ? HX_GQA_TILES_BF16 : (FMT == 1 ? HX_GQA_TILES_FP8 : HX_GQA_TILES_FP4);
-constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr float kLn2 = 0.693147180559945309f;
 // log2 of the largest unnormalised probability (see chunk_step).  bf16
@@ -357,8 +355,10 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
 }
 
-template <int FMT, bool PAGED>
-__global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs a) {
+template <int FMT, bool PAGED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialArgs a) {
+  constexpr int kWaves = WAVES;
+  constexpr int kThreads = 64 * kWaves;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15;   // head column / token row inside a fragment
@@ -557,6 +557,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const PartialArgs
 
 }
 
+template <int FMT, bool PAGED>
+void launch_fmt(const PartialArgs& a, int nwg, hipStream_t st) {
+  if (a.waves == kGqaShortWaves)
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaShortWaves>), dim3(nwg), dim3(64 * kGqaShortWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaWavesPerWg>), dim3(nwg), dim3(64 * kGqaWavesPerWg), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st) {
@@ -565,22 +573,13 @@ hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st) {
   const bool paged = a.table != nullptr;
   switch (dtype) {
     case HX_KV_BF16:
-      if (paged)
-        hipLaunchKernelGGL((gqa_partial_kernel<0, true>), dim3(nwg), dim3(kThreads), 0, st, a);
-      else
-        hipLaunchKernelGGL((gqa_partial_kernel<0, false>), dim3(nwg), dim3(kThreads), 0, st, a);
+      paged ? launch_fmt<0, true>(a, nwg, st) : launch_fmt<0, false>(a, nwg, st);
       break;
     case HX_KV_FP8_E4M3:
-      if (paged)
-        hipLaunchKernelGGL((gqa_partial_kernel<1, true>), dim3(nwg), dim3(kThreads), 0, st, a);
-      else
-        hipLaunchKernelGGL((gqa_partial_kernel<1, false>), dim3(nwg), dim3(kThreads), 0, st, a);
+      paged ? launch_fmt<1, true>(a, nwg, st) : launch_fmt<1, false>(a, nwg, st);
       break;
     default:
-      if (paged)
-        hipLaunchKernelGGL((gqa_partial_kernel<2, true>), dim3(nwg), dim3(kThreads), 0, st, a);
-      else
-        hipLaunchKernelGGL((gqa_partial_kernel<2, false>), dim3(nwg), dim3(kThreads), 0, st, a);
+      paged ? launch_fmt<2, true>(a, nwg, st) : launch_fmt<2, false>(a, nwg, st);
       break;
   }
   return hipGetLastError();

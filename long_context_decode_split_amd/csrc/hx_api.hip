@@ -600,7 +600,9 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     // short contexts: slices of at most kShortSliceChunks tiles are not split
     // (one workgroup per slice, no fold launch; measured faster on the
     // 4,096-token single-request step, where fixed launch costs dominate)
-    if (nch_max <= kShortSliceChunks) cpw = std::max<int64_t>(cpw, nch_max);
+    const bool short_mode = nch_max <= kShortSliceChunks;
+    if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
+    a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
     if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
     a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
     int wgs = 0, folds = 0;

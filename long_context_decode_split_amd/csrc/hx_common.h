@@ -218,6 +218,7 @@ struct PartialArgs {
   float c2;                // softmax scale * log2(e)
   int split_p;             // MLA: P as bf16 high part + residual (else rounded once)
   int cpw;                 // chunks per workgroup (split size)
+  int waves;               // GQA: waves per workgroup (kGqaWavesPerWg, or kGqaShortWaves for unsplit slices)
   int64_t n[kMaxBatchPerLaunch];
   int nsplit[kMaxBatchPerLaunch];
   int wg_begin[kMaxBatchPerLaunch + 1];     // first workgroup (= split record) of each request
@@ -241,6 +242,12 @@ hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part,
 
 // Split policy shared by hx_workspace_size and hx_decode_attn_partial.
 constexpr int kGqaWavesPerWg = 4;
+// Short slices (not split) are latency-bound: their one workgroup per slice
+// gets more waves, each with fewer tiles in its chain.
+#ifndef HX_GQA_SHORT_WAVES
+#define HX_GQA_SHORT_WAVES 8
+#endif
+constexpr int kGqaShortWaves = HX_GQA_SHORT_WAVES;
 constexpr int kGqaTargetWgs = 2048;   // upper bound on the split target
 constexpr int kMlaTargetWgs = 1024;
 constexpr int kMaxSplits = 256;       // splits per slice (the fold keeps their weights in LDS)
