@@ -157,6 +157,34 @@ HXHD void tile_inv(int lay, int width, int64_t off2, int* m, int* d) {
   }
 }
 
+// Rows [*mlo, *mhi] that the 16-byte piece at byte0 of a tile can hold
+// (a superset: the exact test follows).
+HXHD void piece_rows(int lay, int width, int64_t byte0, int nbytes, int* mlo, int* mhi) {
+  const int b = (int)byte0;
+  switch (lay) {
+    case kLayGqaBf16K:
+    case kLayGqaFp8K:
+    case kLayGqaFp4K:   // lane l = 16 h + m holds one token m
+      *mlo = *mhi = (b >> 4) & 15;
+      return;
+    case kLayGqaBf16V:
+    case kLayGqaFp8V:
+    case kLayGqaFp4V: {   // lane l = 16 hq + c holds tokens 4 hq .. 4 hq + 3
+      const int hq = ((b >> 4) & 63) >> 4;
+      *mlo = 4 * hq;
+      *mhi = 4 * hq + 3;
+      return;
+    }
+    case kLayMlaBf16:     // pieces never straddle a 1,152-byte row
+      *mlo = *mhi = b / (width * 2);
+      return;
+    default:              // row-major bytes
+      *mlo = b / width;
+      *mhi = (b + nbytes - 1) / width;
+      return;
+  }
+}
+
 // ---------------------------------------------------------------- tile addressing
 // Dense cache: tile (slice r, request b, KV head g, local 16-row group c) is
 // tile ((r * B + b) * Hkv + g) * cap_chunks + c of every plane.  Block pool:

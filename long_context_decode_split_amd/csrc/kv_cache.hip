@@ -29,13 +29,28 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
     pieces[p] = a.ebits[p] == 32 ? 1 : (a.tile_bytes[p] + 15) / 16;
     piece_sum += pieces[p];
   }
-  int64_t t = gid;
-  int64_t piece = t % piece_sum;
-  t /= piece_sum;
-  const int ci = (int)(t % a.max_chunks);
-  t /= a.max_chunks;
-  const int g = (int)(t % a.Hkv);
-  const int bl = (int)(t / a.Hkv);
+  // thread -> (request, head, chunk, piece); 32-bit division when the grid
+  // allows it (64-bit division is a long software sequence on the GPU)
+  int64_t piece;
+  int ci, g, bl;
+  if (total <= 0xffffffffll) {
+    uint32_t t = (uint32_t)gid;
+    const uint32_t ps = (uint32_t)piece_sum, mc = (uint32_t)a.max_chunks, hk = (uint32_t)a.Hkv;
+    piece = t % ps;
+    t /= ps;
+    ci = (int)(t % mc);
+    t /= mc;
+    g = (int)(t % hk);
+    bl = (int)(t / hk);
+  } else {
+    int64_t t = gid;
+    piece = t % piece_sum;
+    t /= piece_sum;
+    ci = (int)(t % a.max_chunks);
+    t /= a.max_chunks;
+    g = (int)(t % a.Hkv);
+    bl = (int)(t / a.Hkv);
+  }
   int plane = 0;
   while (piece >= pieces[plane]) piece -= pieces[plane++];
 
@@ -45,8 +60,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   const int64_t c = pos / kChunk + ci;           // request-level chunk (group) index
   const int64_t row0 = c * kChunk;
   if (end == pos || row0 >= end) return;   // nothing of this request lands in this chunk
-  const int r = (int)(c % a.P);
-  const int64_t lc = c / a.P;
+  int r;
+  int64_t lc;
+  if (c <= 0xffffffffll) {
+    r = (int)((uint32_t)c % (uint32_t)a.P);
+    lc = (uint32_t)c / (uint32_t)a.P;
+  } else {
+    r = (int)(c % a.P);
+    lc = c / a.P;
+  }
   const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, lc);
   const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new;   // token-major source, this launch's rows
   const uint8_t* src = a.src[plane];
@@ -69,7 +91,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   auto elem_off2 = [&](int e) -> int64_t {
     return eb == 16 ? 2 * (byte0 + 2 * e) : (eb == 8 ? 2 * (byte0 + e) : 2 * byte0 + e);
   };
-  // a piece holding none of the new rows stays as it is
+  // a piece holding none of the new rows stays as it is: first a cheap test
+  // on the piece's row range, then the exact one
+  {
+    int mlo, mhi;
+    piece_rows(lay, width, byte0, nbytes, &mlo, &mhi);
+    if (row0 + mhi < pos || row0 + mlo >= end) return;
+  }
   bool any = false;
   for (int e = 0; e < nelem; ++e) {
     int mm, d;
@@ -78,6 +106,22 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   }
   if (!any) return;
   const bool whole = row0 >= pos && row0 + kChunk <= end;
+  if (!whole && eb != 4) {
+    // part of the piece is new (a decode step's row): store just the new
+    // 1- or 2-byte elements, so the stored bytes of other rows are not read
+    for (int e = 0; e < nelem; ++e) {
+      int mm, d;
+      tile_inv(lay, width, elem_off2(e), &mm, &d);
+      const int64_t tok = row0 + mm;
+      if (tok < pos || tok >= end) continue;
+      const uint8_t* srcrow = src + (src_tok0 + (tok - pos)) * srow;
+      if (eb == 16)
+        *reinterpret_cast<uint16_t*>(dst + byte0 + 2 * e) = *reinterpret_cast<const uint16_t*>(srcrow + 2 * d);
+      else
+        dst[byte0 + e] = srcrow[d];
+    }
+    return;
+  }
   uint8_t buf[16];
   if (nbytes == 16) {
     const uint4 v = whole ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(dst + byte0);
