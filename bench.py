@@ -176,9 +176,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--append", choices=("codes", "bf16"), default="codes",
+    ap.add_argument("--append", choices=("codes", "bf16", "fused"), default="codes",
                     help="codes: the step appends the newest token in storage format (hx_kv_append); bf16: as bf16 "
-                         "values quantised on the device (hx_kv_append_bf16)")
+                         "values quantised on the device (hx_kv_append_bf16); fused: the whole step is one "
+                         "hx_decode_step call (append inside the partial kernel, final O and LSE)")
     ap.add_argument("--attn", choices=("partial+combine", "one-call"), default="partial+combine",
                     help="partial+combine: hx_decode_attn_partial then hx_lse_combine (the slice partials are "
                          "outputs); one-call: hx_decode_attn (final O and LSE only; one launch for small problems)")
@@ -225,8 +226,17 @@ def main():
     append_codes = api.kv_append_paged if paged else api.kv_append
     attn_one = api.decode_attn_paged if paged else api.decode_attn
     attn_partial = api.decode_attn_partial_paged if paged else api.decode_attn_partial
+    fused_step = api.decode_step_paged if paged else api.decode_step
 
     def step(ev=None, stream=stream):
+        if args.append == "fused":
+            if ev is not None:
+                ev[0].record(stream)
+            fused_step(cache, st["k"], st["v"], st["ks"], st["vs"], inp.q, inp.ctx, w.softmax_scale, o, lse, ws,
+                       stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if args.append == "bf16":
             append_bf16(cache, st["kb"], st["vb"], pos=st["pos"], stream=stream)
         else:
@@ -328,8 +338,9 @@ def main():
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "Dk": w.Dk, "Dv": w.Dv,
             "v_alias_k": w.v_alias_k, "kv_dtype": w.dtype, "slices": w.P,
             "context": inp.ctx if w.ctx is None else w.ctx, "kv_bytes_per_step": nbytes, "seed": args.seed,
-            "append": "bf16 values quantised on the device" if args.append == "bf16" else "storage format",
-            "attention": args.attn,
+            "append": {"bf16": "bf16 values quantised on the device", "codes": "storage format",
+                       "fused": "storage format, inside the attention call (hx_decode_step)"}[args.append],
+            "attention": "one-call" if args.append == "fused" else args.attn,
             "layout": "block pool, 16-row blocks shuffled within each request" if paged else "dense planes",
             "launch": "one HIP graph replay per step" if args.graph else "eager launches",
             "p_in_value_product": ("bf16, rounded once" if args.p_bf16 or w.dtype != "bf16"
@@ -337,7 +348,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("decode_attn" if args.attn == "one-call" else "decode_attn_partial") + ("_paged" if paged else ""),
+            "kernel": ("decode_step" if args.append == "fused" else "decode_attn" if args.attn == "one-call"
+                       else "decode_attn_partial") + ("_paged" if paged else ""),
             "achieved": round(kern_gbs, 2),
             "peak": peak_gbs,
             "unit": "GB/s",

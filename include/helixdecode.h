@@ -237,6 +237,22 @@ hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const
                          const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* A whole decode step in one call for callers that hold all slices on one
+ * GPU: append each request's n_new newest rows, then hx_decode_attn.  The
+ * new rows are rows [ctx_len[b] - n_new, ctx_len[b]) of request b, given in
+ * storage format as for hx_kv_append (k_new [B][Hkv][n_new][..] etc., count
+ * = n_new for every request; requires ctx_len[b] >= n_new >= 1); O, LSE,
+ * workspace and the other arguments as hx_decode_attn.  The append runs
+ * inside the partial kernel: the workgroup that owns a new row's chunk tile
+ * writes the row before it reads the tile (one launch fewer than append +
+ * attention; the cache afterwards holds exactly what hx_kv_append writes).
+ * Helix summary, paragraphs on Helix's two layouts (new KV written
+ * round-robin as produced) and on KV parallelism. */
+hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                         const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q, int32_t Hq,
+                         const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* LSE-weighted combine of P partials (jaehun.me review, Prompt 1.3.2):
  *   m = max_r LSE_r, w_r = exp(LSE_r - m),
  *   o = sum_r w_r O_r / sum_r w_r,  lse = m + ln sum_r w_r.
@@ -306,6 +322,12 @@ hx_status hx_decode_attn_partial_paged(const hx_kv_desc* desc, const hx_kv_pool*
 hx_status hx_decode_attn_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,
                                const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* hx_decode_step on a pool cache (the new rows' blocks must be listed). */
+hx_status hx_decode_step_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new, const void* v_new,
+                               const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q,
+                               int32_t Hq, const int64_t* ctx_len, float scale, float* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Host-side block allocator for a pool of num_blocks blocks: a free list
  * that hands out the most recently freed block first (initially 0, 1, ...).

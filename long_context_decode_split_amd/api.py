@@ -18,7 +18,8 @@ from ._lib import (HX_FLAG_P_BF16, HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXEr
 __all__ = ["HXError", "HX_FLAG_P_BF16", "KVDesc", "KVCache", "KVPool", "DTYPES", "kv_layout", "pool_layout", "slot", "slice_len",
            "kv_tile_offset", "kv_append", "kv_append_bf16", "kv_dequant", "kv_append_paged", "kv_append_bf16_paged",
            "kv_dequant_paged", "workspace_size", "workspace_init", "decode_attn_partial", "decode_attn",
-           "decode_attn_partial_paged", "decode_attn_paged", "lse_combine", "version", "exported_symbols"]
+           "decode_attn_partial_paged", "decode_attn_paged", "decode_step", "decode_step_paged", "lse_combine",
+           "version", "exported_symbols"]
 
 DTYPES = {"bf16": HX_KV_BF16, "fp8_e4m3": HX_KV_FP8_E4M3, "mxfp4": HX_KV_MXFP4}
 
@@ -278,6 +279,25 @@ def decode_attn_partial_paged(pool: KVPool, q, ctx_len, scale, o_part, lse_part,
 def decode_attn_paged(pool: KVPool, q, ctx_len, scale, o, lse, ws, stream=None):
     """``hx_decode_attn_paged``: ``decode_attn`` on a block pool."""
     check(lib().hx_decode_attn_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(q), q.shape[1],
+                                     _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_step(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, q, ctx_len, scale, o, lse, ws, stream=None):
+    """``hx_decode_step``: append the newest ``k_new.shape[2]`` rows of every
+    request (storage format, [B, Hkv, n_new, ...]) and attend: o f32
+    [B, Hq, Dv], lse f32 [B, Hq]."""
+    check(lib().hx_decode_step(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+                               _ptr(k_scale_new), _ptr(v_scale_new), k_new.shape[2], _ptr(q), q.shape[1],
+                               _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_step_paged(pool: KVPool, k_new, v_new, k_scale_new, v_scale_new, q, ctx_len, scale, o, lse, ws,
+                      stream=None):
+    """``hx_decode_step_paged``: ``decode_step`` on a block pool."""
+    check(lib().hx_decode_step_paged(ctypes.byref(pool.desc.c()), ctypes.byref(pool.c()), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_scale_new), _ptr(v_scale_new), k_new.shape[2], _ptr(q), q.shape[1],
                                      _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kFoldThreads) void split_fold_kernel(const PartialA
 // the launch folds the partial of every (slice, split) of its group by the
 // same LSE rule, straight into the final output: for a slice with one split
 // the partial kernel wrote the slice output, otherwise the split records.
-constexpr int kFcThreads = 128;
+constexpr int kFcThreads = 256;
 constexpr int kFcMaxItems = kMaxSplits * 64;   // P * nsplit (P <= 64)
 
 __global__ __launch_bounds__(kFcThreads) void fold_combine_kernel(const PartialArgs a, float* __restrict__ o,
@@ -144,9 +144,10 @@ __global__ __launch_bounds__(kFcThreads) void fold_combine_kernel(const PartialA
   auto item_lse = [&](int i) -> float {
     return nsplit == 1 ? a.lse_part[((int64_t)i * a.Btot + b) * a.Hq + hq] : a.ws_lse[(rec0 + i) * G + hd];
   };
-  auto item_o = [&](int i, int d) -> float {
-    return nsplit == 1 ? a.o_part[(((int64_t)i * a.Btot + b) * a.Hq + hq) * Dv + d]
-                       : a.ws_o[((rec0 + i) * G + hd) * Dv + d];
+  auto item_o4 = [&](int i, int d) -> float4 {
+    const float* p = nsplit == 1 ? a.o_part + (((int64_t)i * a.Btot + b) * a.Hq + hq) * Dv + d
+                                 : a.ws_o + ((rec0 + i) * G + hd) * Dv + d;
+    return *reinterpret_cast<const float4*>(p);
   };
   float m = -INFINITY;
   for (int i = tid; i < items; i += kFcThreads) {
@@ -166,13 +167,52 @@ __global__ __launch_bounds__(kFcThreads) void fold_combine_kernel(const PartialA
   __syncthreads();
   float den = 0.f;
   for (int i = 0; i < items; ++i) den += s_w[i];
-  for (int d = tid; d < Dv; d += kFcThreads) {
-    float num = 0.f;
-    for (int i = 0; i < items; ++i) {
-      const float w = s_w[i];
-      if (w != 0.f) num += w * item_o(i, d);
+  // threads split the items into groups; each thread sums 4 consecutive
+  // columns of its group's items with independent 16-byte loads (every
+  // record and slice output is written, so weight-0 items add exact zeros),
+  // then the groups' sums are added in LDS
+  const int lanes = Dv / 4;                  // threads per item group
+  const int groups = kFcThreads / lanes;     // Dv = 128: 8, Dv = 512: 2
+  const int grp = tid / lanes, d4 = 4 * (tid % lanes);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (grp < groups) {
+    int i = grp;
+    for (; i + 3 * groups < items; i += 4 * groups) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = item_o4(i + u * groups, d4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = s_w[i + u * groups];
+        acc.x += w * v[u].x;
+        acc.y += w * v[u].y;
+        acc.z += w * v[u].z;
+        acc.w += w * v[u].w;
+      }
     }
-    o[((int64_t)b * a.Hq + hq) * Dv + d] = den > 0.f ? num / den : 0.f;
+    for (; i < items; i += groups) {
+      const float4 v = item_o4(i, d4);
+      const float w = s_w[i];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+  }
+  __shared__ float4 s_acc[kFcThreads];
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    for (int q = 1; q < groups; ++q) {
+      const float4 t = s_acc[q * lanes + tid];
+      acc.x += t.x;
+      acc.y += t.y;
+      acc.z += t.z;
+      acc.w += t.w;
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    float4* out = reinterpret_cast<float4*>(o + ((int64_t)b * a.Hq + hq) * Dv + d4);
+    *out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
   if (tid == 0) lse[(int64_t)b * a.Hq + hq] = den > 0.f ? m + __log2f(den) * kLn2 : -INFINITY;
 }

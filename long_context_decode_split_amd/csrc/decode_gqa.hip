@@ -26,7 +26,7 @@
 // The rescale of the accumulator runs only on tiles that move a head's
 // reference max (bf16: any growth; fp8 / MXFP4: growth by more than 2^8).
 
-#include "hx_common.h"
+#include "hx_append.h"
 
 namespace hx {
 namespace {
@@ -355,7 +355,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
 }
 
-template <int FMT, bool PAGED, int WAVES>
+template <int FMT, bool PAGED, int WAVES, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialArgs a) {
   constexpr int kWaves = WAVES;
   constexpr int kThreads = 64 * kWaves;
@@ -380,6 +380,7 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
   const int nch = (int)((L + kChunk - 1) / kChunk);
   const int c0 = split * a.cpw;
   const int c1 = min(c0 + a.cpw, nch);
+  if constexpr (FUSED) fused_append(a.app, bl, g, r, c0, c1);   // the step's new rows of these tiles first
   const int tail_valid = (int)(L - (int64_t)(nch - 1) * kChunk);   // rows in the last chunk
 
   // Dense cache: the slice's tiles are consecutive from tile0.  Block pool:
@@ -557,12 +558,22 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
 
 }
 
+template <int FMT, bool PAGED, bool FUSED>
+void launch_waves(const PartialArgs& a, int nwg, hipStream_t st) {
+  if (a.waves == kGqaShortWaves)
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaShortWaves, FUSED>), dim3(nwg), dim3(64 * kGqaShortWaves), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaWavesPerWg, FUSED>), dim3(nwg), dim3(64 * kGqaWavesPerWg), 0,
+                       st, a);
+}
+
 template <int FMT, bool PAGED>
 void launch_fmt(const PartialArgs& a, int nwg, hipStream_t st) {
-  if (a.waves == kGqaShortWaves)
-    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaShortWaves>), dim3(nwg), dim3(64 * kGqaShortWaves), 0, st, a);
+  if (a.fused_append)
+    launch_waves<FMT, PAGED, true>(a, nwg, st);
   else
-    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaWavesPerWg>), dim3(nwg), dim3(64 * kGqaWavesPerWg), 0, st, a);
+    launch_waves<FMT, PAGED, false>(a, nwg, st);
 }
 
 }  // namespace

@@ -40,7 +40,7 @@
 
 #include <type_traits>
 
-#include "hx_common.h"
+#include "hx_append.h"
 
 namespace hx {
 namespace {
@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-template <bool PAGED, bool SPLITP>
+template <bool PAGED, bool SPLITP, bool FUSED>
 __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNBuf][kTileBytes];
@@ -162,6 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   const uint8_t* base = a.k + tile0 * a.k_tile + t_begin * kRowBytes;
   const int32_t* trow = PAGED ? a.table + ((int64_t)b * a.P + r) * a.cap_chunks : nullptr;
   const int64_t cbeg = t_begin / kChunk;   // first 16-row group of the split
+  if constexpr (FUSED) fused_append(a.app, bl, g, r, cbeg, cbeg + (ntok + kChunk - 1) / kChunk);
 
   // ---- Q^T fragments of head 32 wave + col (B operand: step s covers
   //      columns 16 s + 8 half .. +7)
@@ -432,16 +433,16 @@ hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
   const dim3 grid(nwg), block(kThreads);
-  if (a.table) {
-    if (a.split_p)
-      hipLaunchKernelGGL((mla_partial_kernel<true, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((mla_partial_kernel<true, false>), grid, block, 0, st, a);
-  } else {
-    if (a.split_p)
-      hipLaunchKernelGGL((mla_partial_kernel<false, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((mla_partial_kernel<false, false>), grid, block, 0, st, a);
+  const int v = (a.table ? 4 : 0) | (a.split_p ? 2 : 0) | (a.fused_append ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((mla_partial_kernel<false, false, false>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((mla_partial_kernel<false, false, true>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((mla_partial_kernel<false, true, false>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((mla_partial_kernel<false, true, true>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((mla_partial_kernel<true, false, false>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((mla_partial_kernel<true, false, true>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((mla_partial_kernel<true, true, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((mla_partial_kernel<true, true, true>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "hx_cache.h"
 
@@ -225,9 +226,11 @@ static hx_status check_pool(const hx_kv_desc* desc, const hx_kv_pool* pool, Pool
   return HX_OK;
 }
 
-static hx_status kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
-                           const void* v_new, const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
-                           const int32_t* count, int32_t n_new, void* stream) {
+// Checks an append's arguments and fills the plane fields of `a` (every
+// request; per-launch fields are set by append_batch).
+static hx_status append_setup(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                              const void* v_new, const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
+                              const int32_t* count, int32_t n_new, AppendArgs* out) {
   if (!desc || !cache || !pos) return fail(HX_EINVAL, "null argument");
   Geometry g;
   hx_status s = geometry(*desc, &g);
@@ -283,21 +286,37 @@ static hx_status kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, Poo
   a.table = pool.table;
   a.num_blocks = pool.num_blocks;
   a.n_new = n_new;
-  const uint8_t* src0[4];
-  for (int p = 0; p < np; ++p) src0[p] = a.src[p];
-  for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
-    const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
-    int maxc = 0;
-    for (int i = 0; i < nb; ++i) {
-      const int64_t p0 = pos[b0 + i];
-      const int32_t cnt = count ? count[b0 + i] : n_new;
-      a.pos[i] = p0;
-      a.count[i] = cnt;
-      if (cnt > 0) maxc = std::max(maxc, (int)((p0 + cnt - 1) / kChunk - p0 / kChunk + 1));
-    }
-    a.max_chunks = maxc;
-    a.b0 = b0;
-    for (int p = 0; p < np; ++p) a.src[p] = src0[p] + (int64_t)b0 * d.Hkv * n_new * a.src_row_bytes[p];
+  *out = a;
+  return HX_OK;
+}
+
+// The per-launch fields of an append for requests b0 .. b0 + nb - 1 (`base`
+// as append_setup left it: its src are the first request's rows).
+static AppendArgs append_batch(const AppendArgs& base, const int64_t* pos, const int32_t* count, int b0, int nb) {
+  AppendArgs a = base;
+  int maxc = 0;
+  for (int i = 0; i < nb; ++i) {
+    const int64_t p0 = pos[b0 + i];
+    const int32_t cnt = count ? count[b0 + i] : base.n_new;
+    a.pos[i] = p0;
+    a.count[i] = cnt;
+    if (cnt > 0) maxc = std::max(maxc, (int)((p0 + cnt - 1) / kChunk - p0 / kChunk + 1));
+  }
+  a.max_chunks = maxc;
+  a.b0 = b0;
+  for (int p = 0; p < a.nplanes; ++p) a.src[p] = base.src[p] + (int64_t)b0 * a.Hkv * a.n_new * a.src_row_bytes[p];
+  return a;
+}
+
+static hx_status kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                           const void* v_new, const void* k_scale_new, const void* v_scale_new, const int64_t* pos,
+                           const int32_t* count, int32_t n_new, void* stream) {
+  AppendArgs base;
+  hx_status s = append_setup(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos, count, n_new, &base);
+  if (s) return s;
+  for (int b0 = 0; b0 < desc->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, desc->B - b0);
+    const AppendArgs a = append_batch(base, pos, count, b0, nb);
     s = check_hip(launch_append(a, nb, (hipStream_t)stream), "kv_append launch");
     if (s) return s;
   }
@@ -522,9 +541,12 @@ namespace hx {
 // The partial pass of a decode step.  With o_final / lse_final (hx_decode_attn)
 // the slice partials go to workspace scratch and one more kernel folds every
 // slice's partial or split records straight into the final output.
+// With `fuse` (an append_setup result) and its host positions, the partial
+// kernels first append those rows into the tiles they own (hx_decode_step).
 static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* q,
                              int32_t Hq, const int64_t* ctx_len, float scale, float* o_part, float* lse_part,
-                             void* ws, size_t ws_bytes, void* stream, float* o_final, float* lse_final) {
+                             void* ws, size_t ws_bytes, void* stream, float* o_final, float* lse_final,
+                             const AppendArgs* fuse = nullptr, const int64_t* fuse_pos = nullptr) {
   const bool final_out = o_final != nullptr;
   if (!desc || !cache || !q || !ctx_len || !ws) return fail(HX_EINVAL, "null argument");
   if (final_out ? !lse_final : (!o_part || !lse_part)) return fail(HX_EINVAL, "null argument");
@@ -618,6 +640,8 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     if (wgs > records) return fail(HX_EINVAL, "internal: %d workgroups exceed the %lld workspace records", wgs, (long long)records);
     a.b0 = b0;
     a.nb = nb;
+    a.fused_append = fuse != nullptr;
+    if (fuse) a.app = append_batch(*fuse, fuse_pos, nullptr, b0, nb);
     hipError_t e = geo.kind == 0 ? launch_gqa_partial(a, d.dtype, (hipStream_t)stream)
                                  : launch_mla_partial(a, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
@@ -670,6 +694,57 @@ hx_status hx_decode_attn_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, c
   if (s) return s;
   if (!o) return fail(HX_EINVAL, "null argument");
   return decode_step(desc, &pool->planes, ref, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
+}
+
+}  // extern "C"
+
+namespace hx {
+
+// hx_decode_step: rows [ctx_len[b] - n_new, ctx_len[b]) of every request are
+// the step's new rows; append them inside the partial pass, then fold.
+static hx_status fused_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                            const void* v_new, const void* k_scale_new, const void* v_scale_new, int32_t n_new,
+                            const void* q, int32_t Hq, const int64_t* ctx_len, float scale, float* o, float* lse,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!desc || !ctx_len || !o || !lse) return fail(HX_EINVAL, "null argument");
+  if (desc->B < 1) return fail(HX_EINVAL, "B=%d must be >= 1", desc->B);
+  std::vector<int64_t> pos((size_t)desc->B);
+  for (int b = 0; b < desc->B; ++b) {
+    if (ctx_len[b] < n_new)
+      return fail(HX_EINVAL, "ctx_len[%d]=%lld is shorter than the n_new=%d new rows", b, (long long)ctx_len[b], n_new);
+    pos[(size_t)b] = ctx_len[b] - n_new;
+  }
+  AppendArgs base;
+  hx_status s = append_setup(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos.data(), nullptr, n_new,
+                             &base);
+  if (s) return s;
+  return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse, &base,
+                     pos.data());
+}
+
+}  // namespace hx
+
+extern "C" {
+
+hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                         const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q, int32_t Hq,
+                         const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  g_err[0] = 0;
+  return fused_step(desc, cache, PoolRef{nullptr, 0}, k_new, v_new, k_scale_new, v_scale_new, n_new, q, Hq, ctx_len,
+                    scale, o, lse, ws, ws_bytes, stream);
+}
+
+hx_status hx_decode_step_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new, const void* v_new,
+                               const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q,
+                               int32_t Hq, const int64_t* ctx_len, float scale, float* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return fused_step(desc, &pool->planes, ref, k_new, v_new, k_scale_new, v_scale_new, n_new, q, Hq, ctx_len, scale,
+                    o, lse, ws, ws_bytes, stream);
 }
 
 hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const float* o_part, const float* lse_part,

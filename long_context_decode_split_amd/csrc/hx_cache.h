@@ -7,25 +7,6 @@
 
 namespace hx {
 
-struct AppendArgs {
-  const uint8_t* src[4];   // k codes, v codes, k scales, v scales (token-major)
-  uint8_t* dst[4];         // planes
-  int lay[4];              // tile layout per plane
-  int width[4];            // row width (row layouts)
-  int ebits[4];            // element bits per plane (16, 8, 4; 32 = fp8 group scale)
-  int64_t src_row_bytes[4];
-  int64_t tile_bytes[4];
-  int nplanes;
-  int P, B, Hkv;
-  int64_t cap_chunks;
-  const int32_t* table;    // pool cache block table (null: dense)
-  int32_t num_blocks;
-  int n_new;
-  int max_chunks;          // largest number of chunks one request touches
-  int64_t pos[kMaxBatchPerLaunch];
-  int32_t count[kMaxBatchPerLaunch];
-  int b0;                  // first request of this launch
-};
 hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st);
 
 // Quantising append of bf16 rows into fp8 or MXFP4 planes (D = 128).

@@ -228,6 +228,28 @@ void clear_error();
 hx_status check_hip(hipError_t e, const char* what);
 
 // ---------------------------------------------------------------- launchers
+// Append of storage-format rows (hx_kv_append; also fused into a decode
+// step's partial kernels).
+struct AppendArgs {
+  const uint8_t* src[4];   // k codes, v codes, k scales, v scales (token-major)
+  uint8_t* dst[4];         // planes
+  int lay[4];              // tile layout per plane
+  int width[4];            // row width (row layouts)
+  int ebits[4];            // element bits per plane (16, 8, 4; 32 = fp8 group scale)
+  int64_t src_row_bytes[4];
+  int64_t tile_bytes[4];
+  int nplanes;
+  int P, B, Hkv;
+  int64_t cap_chunks;
+  const int32_t* table;    // pool cache block table (null: dense)
+  int32_t num_blocks;
+  int n_new;
+  int max_chunks;          // largest number of chunks one request touches
+  int64_t pos[kMaxBatchPerLaunch];
+  int32_t count[kMaxBatchPerLaunch];
+  int b0;                  // first request of this launch
+};
+
 struct PartialArgs {
   const uint8_t* k;
   const uint8_t* v;
@@ -245,6 +267,8 @@ struct PartialArgs {
   int64_t k_tile, v_tile, ks_tile, vs_tile;
   float c2;                // softmax scale * log2(e)
   int split_p;             // MLA: P as bf16 high part + residual (else rounded once)
+  int fused_append;        // the workgroups first append app's rows into the tiles they own
+  AppendArgs app;          // (same requests as this launch: app.b0 = b0)
   int cpw;                 // chunks per workgroup (split size)
   int waves;               // GQA: waves per workgroup (kGqaWavesPerWg, or kGqaShortWaves for unsplit slices)
   int64_t n[kMaxBatchPerLaunch];

@@ -1,17 +1,8 @@
-// KV cache writes and reads: append with the 16-token round-robin placement,
+// KV cache writes and reads: append with the 16-token round-robin placement
+// (one thread per 16-byte destination piece, append_piece in hx_append.h),
 // and row dequantisation for inspection.
-//
-// Placement (Helix summary, paragraph on Helix's two layouts; NVIDIA blog,
-// section on distributed KV placement): token t of a request belongs to the
-// 16-token group c = t / 16, which lives in slice c mod P as that slice's
-// (c / P)-th chunk tile.
-//
-// The append kernel owns destination bytes, not source tokens: one thread
-// builds one 16-byte piece of a chunk tile, fetching each element of the
-// piece from the new tokens when its row is being appended and keeping the
-// stored bytes otherwise.  No two threads touch the same bytes, so the result
-// does not depend on scheduling, and bytes move unconverted (bit-exact).
 
+#include "hx_append.h"
 #include "hx_cache.h"
 
 namespace hx {
@@ -24,11 +15,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
   if (gid >= total) return;
 
   // pieces of every plane for one (request, head, chunk)
-  int64_t pieces[4], piece_sum = 0;
-  for (int p = 0; p < a.nplanes; ++p) {
-    pieces[p] = a.ebits[p] == 32 ? 1 : (a.tile_bytes[p] + 15) / 16;
-    piece_sum += pieces[p];
-  }
+  int64_t pieces[4];
+  const int64_t piece_sum = append_pieces(a, pieces);
   // thread -> (request, head, chunk, piece); 32-bit division when the grid
   // allows it (64-bit division is a long software sequence on the GPU)
   int64_t piece;
@@ -51,109 +39,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
     g = (int)(t % a.Hkv);
     bl = (int)(t / a.Hkv);
   }
-  int plane = 0;
-  while (piece >= pieces[plane]) piece -= pieces[plane++];
-
-  const int b = a.b0 + bl;
-  const int64_t pos = a.pos[bl];
-  const int64_t end = pos + a.count[bl];
-  const int64_t c = pos / kChunk + ci;           // request-level chunk (group) index
-  const int64_t row0 = c * kChunk;
-  if (end == pos || row0 >= end) return;   // nothing of this request lands in this chunk
-  int r;
-  int64_t lc;
-  if (c <= 0xffffffffll) {
-    r = (int)((uint32_t)c % (uint32_t)a.P);
-    lc = (uint32_t)c / (uint32_t)a.P;
-  } else {
-    r = (int)(c % a.P);
-    lc = c / a.P;
-  }
-  const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, lc);
-  const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new;   // token-major source, this launch's rows
-  const uint8_t* src = a.src[plane];
-  uint8_t* dst = a.dst[plane] + tile * a.tile_bytes[plane];
-
-  if (a.ebits[plane] == 32) {
-    // one fp32 scale per chunk: taken from the first new token of the chunk
-    const int64_t tf = row0 > pos ? row0 : pos;
-    const float v = reinterpret_cast<const float*>(src)[src_tok0 + (tf - pos)];
-    *reinterpret_cast<float*>(dst) = v;
-    return;
-  }
-
-  const int64_t byte0 = piece * 16;
-  const int nbytes = (int)((a.tile_bytes[plane] - byte0) < 16 ? (a.tile_bytes[plane] - byte0) : 16);
-  const int eb = a.ebits[plane];
-  const int lay = a.lay[plane], width = a.width[plane];
-  const int64_t srow = a.src_row_bytes[plane];
-  const int nelem = eb == 16 ? nbytes / 2 : (eb == 8 ? nbytes : 2 * nbytes);
-  auto elem_off2 = [&](int e) -> int64_t {
-    return eb == 16 ? 2 * (byte0 + 2 * e) : (eb == 8 ? 2 * (byte0 + e) : 2 * byte0 + e);
-  };
-  // a piece holding none of the new rows stays as it is: first a cheap test
-  // on the piece's row range, then the exact one
-  {
-    int mlo, mhi;
-    piece_rows(lay, width, byte0, nbytes, &mlo, &mhi);
-    if (row0 + mhi < pos || row0 + mlo >= end) return;
-  }
-  bool any = false;
-  for (int e = 0; e < nelem; ++e) {
-    int mm, d;
-    tile_inv(lay, width, elem_off2(e), &mm, &d);
-    any |= row0 + mm >= pos && row0 + mm < end;
-  }
-  if (!any) return;
-  const bool whole = row0 >= pos && row0 + kChunk <= end;
-  if (!whole && eb != 4) {
-    // part of the piece is new (a decode step's row): store just the new
-    // 1- or 2-byte elements, so the stored bytes of other rows are not read
-    for (int e = 0; e < nelem; ++e) {
-      int mm, d;
-      tile_inv(lay, width, elem_off2(e), &mm, &d);
-      const int64_t tok = row0 + mm;
-      if (tok < pos || tok >= end) continue;
-      const uint8_t* srcrow = src + (src_tok0 + (tok - pos)) * srow;
-      if (eb == 16)
-        *reinterpret_cast<uint16_t*>(dst + byte0 + 2 * e) = *reinterpret_cast<const uint16_t*>(srcrow + 2 * d);
-      else
-        dst[byte0 + e] = srcrow[d];
-    }
-    return;
-  }
-  uint8_t buf[16];
-  if (nbytes == 16) {
-    const uint4 v = whole ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(dst + byte0);
-    __builtin_memcpy(buf, &v, 16);
-  } else {
-    for (int i = 0; i < nbytes; ++i) buf[i] = dst[byte0 + i];
-  }
-  for (int e = 0; e < nelem; ++e) {
-    int mm, d;
-    tile_inv(lay, width, elem_off2(e), &mm, &d);
-    const int64_t tok = row0 + mm;
-    if (tok < pos || tok >= end) continue;
-    const uint8_t* srcrow = src + (src_tok0 + (tok - pos)) * srow;
-    if (eb == 16) {
-      buf[2 * e] = srcrow[2 * d];
-      buf[2 * e + 1] = srcrow[2 * d + 1];
-    } else if (eb == 8) {
-      buf[e] = srcrow[d];
-    } else {   // 4-bit codes, even element in the low nibble of the source
-      const uint8_t sb = srcrow[d >> 1];
-      const uint8_t code = (d & 1) ? (sb >> 4) : (sb & 0xf);
-      uint8_t& o = buf[e >> 1];
-      o = (e & 1) ? (uint8_t)((o & 0x0f) | (code << 4)) : (uint8_t)((o & 0xf0) | code);
-    }
-  }
-  if (nbytes == 16) {
-    uint4 v;
-    __builtin_memcpy(&v, buf, 16);
-    *reinterpret_cast<uint4*>(dst + byte0) = v;
-  } else {
-    for (int i = 0; i < nbytes; ++i) dst[byte0 + i] = buf[i];
-  }
+  append_piece(a, bl, g, ci, piece);
 }
 
 // fp8 e4m3 code -> fp32 (hardware conversion, OCP e4m3 on gfx950).

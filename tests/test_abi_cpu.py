@@ -206,6 +206,29 @@ def test_decode_attn_argument_checks():
         assert call() == _lib.HX_EHIP             # valid arguments reach the launch
 
 
+def test_decode_step_argument_checks():
+    L = _lib.lib()
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+
+    def call(ctx=(5, 17), n_new=1, o=0x30000, kn=0x70000, vn=0x80000, ks=None):
+        c = (ctypes.c_int64 * 2)(*ctx)
+        return L.hx_decode_step(ctypes.byref(d.c()), ctypes.byref(cache), _fake(kn) if kn else None,
+                                _fake(vn) if vn else None, _fake(ks) if ks else None, None, n_new, _fake(0x10000), 8,
+                                c, ctypes.c_float(0.1), _fake(o) if o else None, _fake(0x40000), _fake(0x20000),
+                                1 << 30, None)
+
+    assert call(ctx=(5, 1), n_new=2) == _lib.HX_EINVAL     # a request shorter than its new rows
+    assert call(n_new=0) == _lib.HX_EINVAL
+    assert call(o=0) == _lib.HX_EINVAL
+    assert call(vn=0) == _lib.HX_EINVAL                    # V rows missing
+    assert call(ks=0x90000) == _lib.HX_EINVAL              # bf16 caches take no scales
+    assert call(kn=0x70004) == _lib.HX_EINVAL              # misaligned
+    assert call(ctx=(5, 4 * 64 + 1)) == _lib.HX_EINVAL     # beyond P * cap
+    if not torch.cuda.is_available():
+        assert call() == _lib.HX_EHIP
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_partial_without_device_is_hx_ehip():
     d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
