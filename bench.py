@@ -1,10 +1,13 @@
 """Decode-step benchmark: split-KV decode attention at a 1M-token context on
 one MI355X.
 
-One step = kv_append of the newest token of every (request, KV head) +
-decode_attn_partial over all slices + lse_combine, on one stream, with the
-cache already resident in HBM.  Inputs are synthetic (seeded), shaped like
-the named workload.  Prints one JSON line.
+One step = the append of the newest token of every (request, KV head) and
+the attention over all slices with their LSE combine, on one stream, with
+the cache already resident in HBM: by default one hx_decode_step call (the
+append inside the partial kernel, then one fold of the slice partials into
+the final O and LSE); --append codes runs hx_kv_append, hx_decode_attn_partial
+and hx_lse_combine as separate calls.  Inputs are synthetic (seeded), shaped
+like the named workload.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
@@ -176,10 +179,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--append", choices=("codes", "bf16", "fused"), default="codes",
-                    help="codes: the step appends the newest token in storage format (hx_kv_append); bf16: as bf16 "
-                         "values quantised on the device (hx_kv_append_bf16); fused: the whole step is one "
-                         "hx_decode_step call (append inside the partial kernel, final O and LSE)")
+    ap.add_argument("--append", choices=("fused", "codes", "bf16"), default="fused",
+                    help="fused (default): the whole step is one hx_decode_step call (the newest token appended in "
+                         "storage format inside the partial kernel, then the final O and LSE); codes: "
+                         "hx_kv_append, then the attention calls of --attn; bf16: as codes, with bf16 values "
+                         "quantised on the device (hx_kv_append_bf16)")
     ap.add_argument("--attn", choices=("partial+combine", "one-call"), default="partial+combine",
                     help="partial+combine: hx_decode_attn_partial then hx_lse_combine (the slice partials are "
                          "outputs); one-call: hx_decode_attn (final O and LSE only; one launch for small problems)")

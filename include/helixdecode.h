@@ -246,8 +246,10 @@ hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const
  * inside the partial kernel: the workgroup that owns a new row's chunk tile
  * writes the row before it reads the tile (one launch fewer than append +
  * attention; the cache afterwards holds exactly what hx_kv_append writes).
- * Helix summary, paragraphs on Helix's two layouts (new KV written
- * round-robin as produced) and on KV parallelism. */
+ * MXFP4 caches take the append kernel first instead (their fused kernel was
+ * slower than the launch it saves).  Helix summary, paragraphs on Helix's
+ * two layouts (new KV written round-robin as produced) and on KV
+ * parallelism. */
 hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
                          const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q, int32_t Hq,
                          const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,

@@ -718,6 +718,11 @@ static hx_status fused_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   hx_status s = append_setup(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos.data(), nullptr, n_new,
                              &base);
   if (s) return s;
+  if (desc->dtype == HX_KV_MXFP4) {   // no fused kernel for MXFP4 (see decode_gqa.hip): append, then attend
+    s = kv_append(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos.data(), nullptr, n_new, stream);
+    if (s) return s;
+    return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
+  }
   return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse, &base,
                      pos.data());
 }
