@@ -605,7 +605,9 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   a.split_p = (d.flags & HX_FLAG_P_BF16) == 0;
   const int64_t records = ws_records(d, geo.kind);
   const int target = target_wgs(geo.kind, d.dtype);
-  const int minc = min_chunks_per_wg(geo.kind);
+  // the one-call forms (fold launched anyway) take splits half as long:
+  // two tiles per wave (measured on the 4,096-token step: 30.2 -> 29.3 us)
+  const int minc = final_out ? std::max(1, min_chunks_per_wg(geo.kind) / 2) : min_chunks_per_wg(geo.kind);
   for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
     int64_t W = 0;
@@ -621,8 +623,11 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
     // short contexts: slices of at most kShortSliceChunks tiles are not split
     // (one workgroup per slice, no fold launch; measured faster on the
-    // 4,096-token single-request step, where fixed launch costs dominate)
-    const bool short_mode = nch_max <= kShortSliceChunks;
+    // 4,096-token single-request step, where fixed launch costs dominate).
+    // The one-call forms fold every record in their second launch anyway, so
+    // there short slices are split like long ones (HX_SHORT_ONE_CALL=1 keeps
+    // them whole: tuning knob).
+    const bool short_mode = nch_max <= kShortSliceChunks && (!final_out || env_int("HX_SHORT_ONE_CALL", 0, 0, 1));
     if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
     a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
     if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
