@@ -22,9 +22,13 @@
 //     scores of head l % 16 for tokens 4*(l/16)..+3, so the row max needs two
 //     lane exchanges and the running sum stays per lane;
 //   * O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16, whose B operand is
-//     the probability fragment exactly as the first product left it.
+//     the probability fragment exactly as the first product left it (bf16
+//     tiles: sixteen, P as a bf16 high part plus its residual).
 // The rescale of the accumulator runs only on tiles that move a head's
 // reference max (bf16: any growth; fp8 / MXFP4: growth by more than 2^8).
+// Template parameters: storage format, dense or block-pool addressing, waves
+// per workgroup (8 for short unsplit slices), and whether the workgroup first
+// appends a decode step's new rows into its tiles (hx_decode_step).
 
 #include "hx_append.h"
 
