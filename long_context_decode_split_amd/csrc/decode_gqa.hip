@@ -259,8 +259,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
 
   // ---- online softmax (base 2)
   float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  cm = fmaxf(cm, __shfl_xor(cm, 16));
-  cm = fmaxf(cm, __shfl_xor(cm, 32));
+  cm = max_xor32(max_xor16(cm));
   // The reference max mrun moves only when some head's scores exceed it by
   // more than kHeadroom: P = 2^(s - mrun) is bounded by 2^kHeadroom, and the
   // rescale of the accumulator (32 multiplies; a factor of exactly 1 for the
@@ -508,10 +507,8 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
   for (int i = 0; i < 8; ++i) acc[i] = st.acc[i];
 
   // ---- fold the lanes' running sums of each head
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  lsum_mfma += __shfl_xor(lsum_mfma, 16);
-  lsum_mfma += __shfl_xor(lsum_mfma, 32);
+  lsum = sum_xor32(sum_xor16(lsum));
+  lsum_mfma = sum_xor32(sum_xor16(lsum_mfma));
 
   // ---- combine the waves of this workgroup (LSE rule, base 2)
   __shared__ float s_m[kWaves][16];

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     float cm = sc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) cm = fmaxf(cm, sc[i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 32)) * c2;
+    cm = max_xor32(cm) * c2;
     mseen = fmaxf(mseen, cm);
     if (mref == -INFINITY) mref = cm;   // first tile of the run (at least one valid token)
 #pragma unroll
@@ -400,8 +400,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   }
 
   // ---- finalize: head 32 wave + col, all 512 value columns
-  lsum += __shfl_xor(lsum, 32);
-  lsum_mfma += __shfl_xor(lsum_mfma, 32);
+  lsum = sum_xor32(lsum);
+  lsum_mfma = sum_xor32(lsum_mfma);
   const int G = a.G;
   const int hd = kHeadsPerWave * wave + col;   // head inside the group
   float* out_o;

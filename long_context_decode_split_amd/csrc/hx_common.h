@@ -55,9 +55,48 @@ enum Layout : int {
 // rows, one piece per half-wave), and maps rows m and m + 2 of an aligned
 // group of 4 to opposite halves of the 8-piece group (the transposed value
 // operand: 4 rows, 4 adjacent pieces).  Measured on gfx950 LDS for the score
-// reads: about 200 B/clk/CU against 62 unswizzled.  Rows copied to LDS
+// reads with eight waves per CU: about 200 B/clk/CU against 62 unswizzled.  Rows copied to LDS
 // unchanged are then read efficiently in both views.
 HXHD int mla_swz(int m) { return 4 * ((m >> 1) & 1) + ((m >> 2) & 3); }
+
+// ---------------------------------------------------------------- lane exchanges
+// x combined with lane l ^ 16 (resp. l ^ 32) of the wave through the gfx950
+// row-swap permutes, VALU instructions without an LDS round trip: with x as
+// both operands, v_permlane16_swap leaves lanes l and l ^ 16 each holding
+// x[l] and x[l ^ 16] across its two results (v_permlane32_swap likewise for
+// l ^ 32), in the same order on both lanes, so both get the same bits.
+__device__ __forceinline__ uint2 swap_rows16(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_uint2(s[0], s[1]);
+#else
+  return make_uint2(__float_as_uint(x), __float_as_uint(x));   // host pass: never called
+#endif
+}
+__device__ __forceinline__ uint2 swap_rows32(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_uint2(s[0], s[1]);
+#else
+  return make_uint2(__float_as_uint(x), __float_as_uint(x));   // host pass: never called
+#endif
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint2 s = swap_rows16(x);
+  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint2 s = swap_rows32(x);
+  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint2 s = swap_rows16(x);
+  return __uint_as_float(s.x) + __uint_as_float(s.y);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint2 s = swap_rows32(x);
+  return __uint_as_float(s.x) + __uint_as_float(s.y);
+}
 
 // Element (row m, column d) -> 2 * byte offset + nibble (nibble is 1 for the
 // high half of an FP4 byte).  `width` is the row width for row layouts.
