@@ -1,9 +1,11 @@
 """Parity at the workloads' full sizes (1M-token contexts; ragged up to 2M),
-in the launch configuration bench.py times: the cache holds n-1 tokens, the
-step appends token n-1, runs the partial kernel over every slice and the
-combine.  The oracle checks sampled (request, KV head) groups over their whole
-context, per slice and combined."""
+in the launch configurations bench.py times.  The cache holds n-1 tokens and
+the step adds token n-1: either as separate calls (append, the partial kernel
+over every slice, the combine; checked per slice and combined) or as one
+hx_decode_step (bench.py's default step).  The oracle checks sampled
+(request, KV head) groups over their whole context."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -65,4 +67,46 @@ def test_full_size_sampled_groups(w, needles, sample):
         worst = H.check_step(inp, o_part, lse_part, o, lse, groups=[grp], heads=heads, label=f"{w.name} {grp}")
         H.log(f"[fullsize]    worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
     del inp, o_part, lse_part, o, lse
+    torch.cuda.empty_cache()
+
+
+STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, configs.DEEPSEEK_MLA]
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda x: x.name)
+def test_full_size_fused_step(w):
+    """bench.py's default step at full size: the cache holds n-1 tokens and
+    one hx_decode_step appends token n-1 inside the partial kernel and folds
+    the slices.  hx_decode_attn over the cache it leaves must give the same
+    bits (the appended rows are what the attention read), and sampled groups
+    must match the oracle."""
+    H.log(f"[fullsize step] {w.name}: generating")
+    inp = synth.make_inputs(w, seed=1, device="cuda", needles=True)
+    cache = H.build_cache(inp, fill=0xFF, upto=[n - 1 for n in inp.ctx])
+    last = [n - 1 for n in inp.ctx]
+    pick = lambda t: None if t is None else torch.stack([t[b, :, last[b]:last[b] + 1] for b in range(w.B)]).contiguous()
+    ws = torch.zeros(api.workspace_size(H.desc_of(inp), w.Hq), dtype=torch.uint8, device="cuda")
+    o1 = torch.full((w.B, w.Hq, w.Dv), float("nan"), device="cuda")
+    l1 = torch.full((w.B, w.Hq), float("nan"), device="cuda")
+    o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
+    H.log(f"[fullsize step] {w.name}: ctx min {min(inp.ctx)} max {max(inp.ctx)}; fused step, then decode_attn")
+    api.decode_step(cache, pick(inp.k), pick(inp.v), pick(inp.k_scale), pick(inp.v_scale), inp.q, inp.ctx,
+                    w.softmax_scale, o2, l2, ws)
+    api.decode_attn(cache, inp.q, inp.ctx, w.softmax_scale, o1, l1, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)) and torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    oc, lc = o2.cpu().numpy(), l2.cpu().numpy()
+    del cache, ws
+    if w.name == configs.MXFP4_RAGGED.name:
+        groups = [(min(range(w.B), key=lambda b: inp.ctx[b]), 0), (max(range(w.B), key=lambda b: inp.ctx[b]), 0)]
+    else:
+        groups = [(0, 0), (w.B - 1, w.Hkv - 1)]
+    heads = np.array(MLA_HEADS) if w.G == 128 else np.arange(w.G)
+    for b, g in groups:
+        H.log(f"[fullsize step] {w.name}: oracle on group {(b, g)} (n={inp.ctx[b]})")
+        _, _, O, L = H.oracle_group(inp, b, g, heads)
+        cols = g * w.G + heads
+        e = H.compare(f"{w.name} fused step b={b} g={g}", oc[b, cols], lc[b, cols], O, L, w.dtype)
+        H.log(f"[fullsize step]    |dO|={e[0]:.2e} LSE rel={e[1]:.2e}")
+    del inp
     torch.cuda.empty_cache()
