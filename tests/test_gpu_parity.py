@@ -87,7 +87,7 @@ def _oracle_rows(inp, b, g):
             V = K[:, :w.Dv]
         return K, V
     K, V = H.token_values(inp, b, g)
-    # MXFP4 values beyond the fp32 range (E = 254 with codes 3..6) become +-inf, as the fp32 dequantisation gives
+    # MXFP4 values beyond the fp32 range (E = 254 with magnitudes 2 to 6) become +-inf, as the fp32 dequantisation gives
     with np.errstate(over="ignore"):
         return K.astype(np.float32), V.astype(np.float32)
 
