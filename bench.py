@@ -213,8 +213,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the KV-parallel slices of this build are slices of one GPU's HBM, and "
-              "no collectives are built; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: every KV-parallel slice lives in that GPU's HBM and the library has "
+              "no collectives between GPUs; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
