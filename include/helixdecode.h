@@ -16,6 +16,13 @@
  * On one GPU every KV-parallel rank becomes one slice of an HBM-resident
  * cache, and the exchange becomes an in-HBM combine (hx_lse_combine).
  *
+ * Short page names used in the citations of this library's sources:
+ * "Helix summary" is the fdeinterviews.com page named above; "jaehun.me
+ * review" the jaehun.me paper review of the same work (sections numbered
+ * Prompt 1.1.1 ... 1.5.2 as on that page); "NVIDIA blog" the open-lab.net
+ * NVIDIA technical blog post (Korean) on multi-million-token real-time
+ * inference; "ifai.io article" the ifai.io news article on NVIDIA's Helix.
+ *
  * Conventions for every entry point
  * ---------------------------------
  *  - Every function returns an hx_status; HX_OK is 0.  Arguments are checked
