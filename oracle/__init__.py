@@ -19,6 +19,11 @@ Sources (the web pages about Helix Parallelism that define the method):
 * open-lab.net (NVIDIA technical blog, Korean), section on distributed KV
   placement: with two KV-parallel ranks, tokens 1-16 go to rank 0 and tokens
   17-32 to rank 1.
+* ifai.io news article on NVIDIA's Helix, section "Decoupling attention and
+  FFN".
+
+The modules cite these pages as "Helix summary", "jaehun.me review", "NVIDIA
+blog" and "ifai.io article".
 
 Modules
 -------
