@@ -102,9 +102,13 @@ typedef struct {
  *               coalesced reads); hx_kv_tile_offset() documents it.  Write
  *               with hx_kv_append, read rows back with hx_kv_dequant.
  *   k_scale,  : HX_KV_FP8_E4M3: float [P][B][Hkv][cap/16] (one per tile);
- *   v_scale     HX_KV_MXFP4: uint8 e8m0 [P][B][Hkv][cap][D/32] (row-major);
- *               HX_KV_BF16: unused (NULL).
- * v and v_scale are NULL when v_alias_k = 1. */
+ *   v_scale     HX_KV_BF16: unused (NULL).
+ * v and v_scale are NULL when v_alias_k = 1.
+ * HX_KV_MXFP4 caches are one plane, passed as k (v, k_scale and v_scale
+ * NULL): each [P][B][Hkv][cap/16] chunk tile of 2,176 bytes holds the K
+ * codes (1,024 B), the V codes (1,024 B), then the e8m0 exponents of K and
+ * of V (16 rows x D/32 bytes each, row-major), so the attention streams one
+ * contiguous run per slice. */
 typedef struct {
   void* k;
   void* v;
@@ -112,10 +116,11 @@ typedef struct {
   void* v_scale;
 } hx_kv_cache;
 
-/* Byte sizes the caller allocates for each plane, and the tile sizes. */
+/* Byte sizes the caller allocates for each plane (0: the plane is absent,
+ * pass NULL), and the tile sizes. */
 typedef struct {
   size_t k_bytes, v_bytes, k_scale_bytes, v_scale_bytes;
-  size_t k_tile_bytes, v_tile_bytes; /* bytes of one 16-row chunk tile */
+  size_t k_tile_bytes, v_tile_bytes; /* bytes of one 16-row chunk tile (MXFP4: the whole packed tile) */
   int64_t n_max;                     /* largest context: P * cap */
 } hx_kv_layout_info;
 
@@ -143,8 +148,12 @@ hx_status hx_slice_len(int64_t n, int32_t P, int32_t r, int64_t* len);
 
 /* Byte offset (times 2, plus 1 for the high nibble of an FP4 code) of
  * element (row m of the tile, column d) inside a chunk tile of the K
- * (which = 0) or V (which = 1) plane.  Host only; documents the tile
- * layout for callers that write tiles themselves. */
+ * (which = 0) or V (which = 1) codes, or of the byte that starts its scale
+ * (which = 2 for K, 3 for V: fp8 the tile's float, MXFP4 the e8m0 of
+ * row m, columns d / 32 * 32 ..); offsets of an MXFP4 cache count from the
+ * start of its packed tile, the others from the tile of their own plane.
+ * HX_EINVAL for scales of a bf16 cache or V of an aliased one.  Host only;
+ * documents the tile layout for callers that write tiles themselves. */
 hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, int32_t d, int64_t* off2);
 
 /* Append new tokens for every KV head, placing each by hx_slot: request b
@@ -285,8 +294,10 @@ hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const flo
  * slice, 16-row group).  Planes of a pool of N blocks (device, caller-owned,
  * sizes from hx_pool_layout):
  *   k, v       : [N][Hkv] chunk tiles, tile byte order as in the dense cache;
- *   k_scale,   : fp8: float [N][Hkv]; MXFP4: uint8 e8m0 [N][Hkv][16][D/32];
- *   v_scale      bf16: NULL.  v and v_scale are NULL when v_alias_k = 1.
+ *   k_scale,   : fp8: float [N][Hkv]; bf16: NULL.
+ *   v_scale      v and v_scale are NULL when v_alias_k = 1.
+ *   MXFP4: one plane k of [N][Hkv] packed 2,176-byte tiles as in the dense
+ *   cache (v, k_scale, v_scale NULL).
  * block_table: device int32 [B][P][cap/16].  Entry (b, r, c) is the block
  *   holding local rows 16c .. 16c+15 of slice r of request b.  desc->cap is
  *   the longest slice a table row can describe (16 entries' worth of rows

@@ -33,6 +33,66 @@ hx_status check_hip(hipError_t e, const char* what) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Plane and tile sizes for `units` chunk tiles per plane (one plane for a
+// packed cache: its tiles hold all four parts).
+static void plane_sizes(const Geometry& g, int64_t units, hx_kv_layout_info* out) {
+  if (g.packed) {
+    out->k_tile_bytes = (size_t)g.packed_tile;
+    out->v_tile_bytes = 0;
+    out->k_bytes = (size_t)(units * g.packed_tile);
+    out->v_bytes = out->k_scale_bytes = out->v_scale_bytes = 0;
+    return;
+  }
+  out->k_tile_bytes = (size_t)g.k_tile;
+  out->v_tile_bytes = (size_t)g.v_tile;
+  out->k_bytes = (size_t)(units * g.k_tile);
+  out->v_bytes = (size_t)(units * g.v_tile);
+  out->k_scale_bytes = (size_t)(units * g.ks_tile);
+  out->v_scale_bytes = (size_t)(units * g.vs_tile);
+}
+
+// The cache as the kernels address it: base pointer and bytes between
+// consecutive chunk tiles of the K codes, V codes, K scales and V scales.
+// A packed (MXFP4) cache is one plane passed as `k`, its tiles holding the
+// four parts in that order; an aliased (MLA) cache reads V from the K plane.
+// Checks which planes must and must not be given, and their alignment.
+struct PlaneRefs {
+  uint8_t* base[4];
+  int64_t stride[4];
+};
+
+static hx_status plane_refs(const hx_kv_desc& d, const Geometry& g, const hx_kv_cache* c, PlaneRefs* out) {
+  PlaneRefs p{};
+  if (!c->k) return fail(HX_EINVAL, "null K plane");
+  if (g.packed) {
+    if (c->v || c->k_scale || c->v_scale)
+      return fail(HX_EINVAL, "an MXFP4 cache is one plane: pass it as k and leave v, k_scale and v_scale NULL");
+    const int64_t off[4] = {0, g.k_tile, g.k_tile + g.v_tile, g.k_tile + g.v_tile + g.ks_tile};
+    for (int i = 0; i < 4; ++i) {
+      p.base[i] = (uint8_t*)c->k + off[i];
+      p.stride[i] = g.packed_tile;
+    }
+  } else {
+    if (d.v_alias_k && c->v) return fail(HX_EINVAL, "cache->v must be NULL when v_alias_k = 1");
+    if (!d.v_alias_k && !c->v) return fail(HX_EINVAL, "null V plane");
+    if (d.dtype != HX_KV_BF16 && (!c->k_scale || (!d.v_alias_k && !c->v_scale)))
+      return fail(HX_EINVAL, "null scale plane");
+    p.base[0] = (uint8_t*)c->k;
+    p.base[1] = (uint8_t*)(d.v_alias_k ? c->k : c->v);
+    p.base[2] = (uint8_t*)c->k_scale;
+    p.base[3] = (uint8_t*)(d.v_alias_k ? c->k_scale : c->v_scale);
+    p.stride[0] = g.k_tile;
+    p.stride[1] = d.v_alias_k ? g.k_tile : g.v_tile;
+    p.stride[2] = g.ks_tile;
+    p.stride[3] = d.v_alias_k ? g.ks_tile : g.vs_tile;
+  }
+  const void* ptrs[4] = {c->k, c->v, c->k_scale, c->v_scale};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  *out = p;
+  return HX_OK;
+}
+
 hx_status geometry(const hx_kv_desc& d, Geometry* g) {
   if (d.P < 1 || d.P > 64) return fail(HX_EINVAL, "P=%d must be in 1..64", d.P);
   if (d.B < 1) return fail(HX_EINVAL, "B=%d must be >= 1", d.B);
@@ -54,6 +114,8 @@ hx_status geometry(const hx_kv_desc& d, Geometry* g) {
     } else {
       t.lay_k = kLayGqaFp4K; t.lay_v = kLayGqaFp4V; t.ebits = 4;
       t.k_tile = t.v_tile = 1024; t.ks_tile = t.vs_tile = 16 * (128 / 32);
+      t.packed = true;
+      t.packed_tile = t.k_tile + t.v_tile + t.ks_tile + t.vs_tile;   // 2,176 B
     }
   } else if (d.Dk == 576 && d.Dv == 512 && d.v_alias_k && d.dtype == HX_KV_BF16) {
     t.kind = 1;
@@ -64,7 +126,7 @@ hx_status geometry(const hx_kv_desc& d, Geometry* g) {
                 d.dtype);
   }
   const double tiles = (double)d.P * d.B * d.Hkv * (double)(d.cap / kChunk);
-  if (tiles * (double)t.k_tile > 9.0e18) return fail(HX_EINVAL, "cache too large");
+  if (tiles * (double)(t.packed ? t.packed_tile : t.k_tile) > 9.0e18) return fail(HX_EINVAL, "cache too large");
   t.tiles = (int64_t)d.P * d.B * d.Hkv * (d.cap / kChunk);
   *g = t;
   return HX_OK;
@@ -160,12 +222,7 @@ hx_status hx_kv_layout(const hx_kv_desc* desc, hx_kv_layout_info* out) {
   Geometry g;
   hx_status s = geometry(*desc, &g);
   if (s) return s;
-  out->k_tile_bytes = (size_t)g.k_tile;
-  out->v_tile_bytes = (size_t)g.v_tile;
-  out->k_bytes = (size_t)(g.tiles * g.k_tile);
-  out->v_bytes = (size_t)(g.tiles * g.v_tile);
-  out->k_scale_bytes = (size_t)(g.tiles * g.ks_tile);
-  out->v_scale_bytes = (size_t)(g.tiles * g.vs_tile);
+  plane_sizes(g, g.tiles, out);
   out->n_max = (int64_t)desc->P * desc->cap;
   return HX_OK;
 }
@@ -194,11 +251,21 @@ hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, in
   Geometry g;
   hx_status s = geometry(*desc, &g);
   if (s) return s;
-  if (which != 0 && which != 1) return fail(HX_EINVAL, "which must be 0 (K) or 1 (V)");
-  const int width = which == 0 ? desc->Dk : desc->Dv;
+  if (which < 0 || which > 3) return fail(HX_EINVAL, "which must be 0 (K), 1 (V), 2 (K scale) or 3 (V scale)");
+  const bool is_v = which == 1 || which == 3;
+  if (is_v && desc->v_alias_k) return fail(HX_EINVAL, "an aliased cache has no V plane");
+  const int width = is_v ? desc->Dv : desc->Dk;
   if (m < 0 || m >= kChunk || d < 0 || d >= width) return fail(HX_EINVAL, "element out of the tile");
-  const int lay = (which == 1 && !desc->v_alias_k) ? g.lay_v : g.lay_k;
-  *off2 = tile_off2(lay, desc->Dk, m, d);
+  if (which < 2) {
+    // a packed tile holds the V codes after the K codes
+    *off2 = tile_off2(is_v ? g.lay_v : g.lay_k, desc->Dk, m, d) + (g.packed && is_v ? 2 * g.k_tile : 0);
+    return HX_OK;
+  }
+  if (desc->dtype == HX_KV_BF16) return fail(HX_EINVAL, "bf16 caches have no scales");
+  // fp8: the tile's one float; MXFP4: the e8m0 byte of row m, 32-column block d / 32 (after the codes when packed)
+  const int64_t byte = desc->dtype == HX_KV_FP8_E4M3 ? 0 : (int64_t)m * (width / 32) + d / 32;
+  const int64_t base = g.packed ? g.k_tile + g.v_tile + (is_v ? g.ks_tile : 0) : 0;
+  *off2 = 2 * (base + byte);
   return HX_OK;
 }
 
@@ -221,7 +288,8 @@ static hx_status check_pool(const hx_kv_desc* desc, const hx_kv_pool* pool, Pool
   Geometry g;
   hx_status s = geometry(*desc, &g);
   if (s) return s;
-  if ((double)pool->num_blocks * desc->Hkv * (double)g.k_tile > 9.0e18) return fail(HX_EINVAL, "pool too large");
+  if ((double)pool->num_blocks * desc->Hkv * (double)(g.packed ? g.packed_tile : g.k_tile) > 9.0e18)
+    return fail(HX_EINVAL, "pool too large");
   *ref = PoolRef{pool->block_table, pool->num_blocks};
   return HX_OK;
 }
@@ -239,13 +307,15 @@ static hx_status append_setup(const hx_kv_desc* desc, const hx_kv_cache* cache, 
   if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
   const bool alias = d.v_alias_k;
   const bool scaled = d.dtype != HX_KV_BF16;
-  if (!cache->k || !k_new) return fail(HX_EINVAL, "null K plane or k_new");
-  if (!alias && (!cache->v || !v_new)) return fail(HX_EINVAL, "null V plane or v_new");
-  if (alias && (v_new || cache->v)) return fail(HX_EINVAL, "v_new and cache->v must be NULL when v_alias_k = 1");
-  if (scaled && (!cache->k_scale || !k_scale_new || (!alias && (!cache->v_scale || !v_scale_new))))
-    return fail(HX_EINVAL, "null scale plane or scale input");
+  PlaneRefs pr;
+  s = plane_refs(d, g, cache, &pr);
+  if (s) return s;
+  if (!k_new) return fail(HX_EINVAL, "null k_new");
+  if (!alias && !v_new) return fail(HX_EINVAL, "null v_new");
+  if (alias && v_new) return fail(HX_EINVAL, "v_new must be NULL when v_alias_k = 1");
+  if (scaled && (!k_scale_new || (!alias && !v_scale_new))) return fail(HX_EINVAL, "null scale input");
   if (!scaled && (k_scale_new || v_scale_new)) return fail(HX_EINVAL, "bf16 caches take no scales");
-  const void* ptrs[8] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_new, v_new, k_scale_new, v_scale_new};
+  const void* ptrs[4] = {k_new, v_new, k_scale_new, v_scale_new};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int64_t nmax = (int64_t)d.P * d.cap;
@@ -259,24 +329,26 @@ static hx_status append_setup(const hx_kv_desc* desc, const hx_kv_cache* cache, 
 
   AppendArgs a{};
   int np = 0;
-  auto add = [&](const void* src, void* dst, int lay, int width, int ebits, int64_t row_bytes, int64_t tile_bytes) {
+  // plane i of pr: 0 K codes, 1 V codes, 2 K scales, 3 V scales
+  auto add = [&](const void* src, int i, int lay, int width, int ebits, int64_t row_bytes, int64_t tile_bytes) {
     a.src[np] = (const uint8_t*)src;
-    a.dst[np] = (uint8_t*)dst;
+    a.dst[np] = pr.base[i];
     a.lay[np] = lay;
     a.width[np] = width;
     a.ebits[np] = ebits;
     a.src_row_bytes[np] = row_bytes;
     a.tile_bytes[np] = tile_bytes;
+    a.tile_stride[np] = pr.stride[i];
     ++np;
   };
-  add(k_new, cache->k, g.lay_k, d.Dk, g.ebits, (int64_t)d.Dk * g.ebits / 8, g.k_tile);
-  if (!alias) add(v_new, cache->v, g.lay_v, d.Dv, g.ebits, (int64_t)d.Dv * g.ebits / 8, g.v_tile);
+  add(k_new, 0, g.lay_k, d.Dk, g.ebits, (int64_t)d.Dk * g.ebits / 8, g.k_tile);
+  if (!alias) add(v_new, 1, g.lay_v, d.Dv, g.ebits, (int64_t)d.Dv * g.ebits / 8, g.v_tile);
   if (d.dtype == HX_KV_FP8_E4M3) {
-    add(k_scale_new, cache->k_scale, kLayRowU8, 1, 32, 4, 4);
-    if (!alias) add(v_scale_new, cache->v_scale, kLayRowU8, 1, 32, 4, 4);
+    add(k_scale_new, 2, kLayRowU8, 1, 32, 4, 4);
+    if (!alias) add(v_scale_new, 3, kLayRowU8, 1, 32, 4, 4);
   } else if (d.dtype == HX_KV_MXFP4) {
-    add(k_scale_new, cache->k_scale, kLayRowU8, d.Dk / 32, 8, d.Dk / 32, g.ks_tile);
-    if (!alias) add(v_scale_new, cache->v_scale, kLayRowU8, d.Dv / 32, 8, d.Dv / 32, g.vs_tile);
+    add(k_scale_new, 2, kLayRowU8, d.Dk / 32, 8, d.Dk / 32, g.ks_tile);
+    if (!alias) add(v_scale_new, 3, kLayRowU8, d.Dv / 32, 8, d.Dv / 32, g.vs_tile);
   }
   a.nplanes = np;
   a.P = d.P;
@@ -334,11 +406,11 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
   if (d.dtype == HX_KV_BF16) return kv_append(desc, cache, pool, k_new, v_new, nullptr, nullptr, pos, count, n_new, stream);
   if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
   // quantised caches are GQA caches (Dk = Dv = 128, separate V)
-  if (!cache->k || !k_new || !cache->v || !v_new) return fail(HX_EINVAL, "null K/V plane or input");
-  if (!cache->k_scale || !cache->v_scale) return fail(HX_EINVAL, "null scale plane");
-  const void* ptrs[6] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_new, v_new};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  PlaneRefs pr;
+  s = plane_refs(d, g, cache, &pr);
+  if (s) return s;
+  if (!k_new || !v_new) return fail(HX_EINVAL, "null k_new or v_new");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int64_t nmax = (int64_t)d.P * d.cap;
   for (int b = 0; b < d.B; ++b) {
     const int32_t cnt = count ? count[b] : n_new;
@@ -348,10 +420,10 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
                   (long long)nmax);
   }
   QAppendArgs a{};
-  a.dst[0] = (uint8_t*)cache->k;
-  a.dst[1] = (uint8_t*)cache->v;
-  a.sc[0] = (uint8_t*)cache->k_scale;
-  a.sc[1] = (uint8_t*)cache->v_scale;
+  a.dst[0] = pr.base[0];
+  a.dst[1] = pr.base[1];
+  a.sc[0] = pr.base[2];
+  a.sc[1] = pr.base[3];
   a.lay[0] = g.lay_k;
   a.lay[1] = g.lay_v;
   a.dtype = d.dtype;
@@ -362,8 +434,8 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
   a.cap_chunks = d.cap / kChunk;
   a.table = pool.table;
   a.num_blocks = pool.num_blocks;
-  a.tile_bytes = g.k_tile;
-  a.sc_tile_bytes = g.ks_tile;
+  a.tile_stride = pr.stride[0];      // K and V code planes share it
+  a.sc_tile_stride = pr.stride[2];   // and so do the scale planes
   a.n_new = n_new;
   for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
@@ -396,17 +468,15 @@ static hx_status kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   const hx_kv_desc& d = *desc;
   if (r < 0 || r >= d.P || b < 0 || b >= d.B || g < 0 || g >= d.Hkv) return fail(HX_EINVAL, "(r, b, g) out of range");
   if (j0 < 0 || n < 0 || j0 + n > d.cap) return fail(HX_EINVAL, "rows [j0, j0+n) must lie in [0, cap)");
-  if (!cache->k || (!d.v_alias_k && !cache->v)) return fail(HX_EINVAL, "null cache plane");
-  if (d.dtype != HX_KV_BF16 && (!cache->k_scale || (!d.v_alias_k && !cache->v_scale)))
-    return fail(HX_EINVAL, "null scale plane");
-  const void* ptrs[6] = {cache->k, cache->v, cache->k_scale, cache->v_scale, k_out, v_out};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  PlaneRefs pr;
+  s = plane_refs(d, geo, cache, &pr);
+  if (s) return s;
+  if (!aligned16(k_out) || (v_out && !aligned16(v_out))) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   DequantArgs a{};
-  a.k = (const uint8_t*)cache->k;
-  a.v = (const uint8_t*)cache->v;
-  a.ks = (const uint8_t*)cache->k_scale;
-  a.vs = (const uint8_t*)cache->v_scale;
+  a.k = pr.base[0];
+  a.v = pr.base[1];
+  a.ks = pr.base[2];
+  a.vs = pr.base[3];
   a.k_out = k_out;
   a.v_out = v_out;
   a.dtype = d.dtype;
@@ -415,10 +485,10 @@ static hx_status kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   a.Dk = d.Dk;
   a.Dv = d.Dv;
   a.v_alias = d.v_alias_k;
-  a.k_tile = geo.k_tile;
-  a.v_tile = geo.v_tile;
-  a.ks_tile = geo.ks_tile;
-  a.vs_tile = geo.vs_tile;
+  a.k_tile = pr.stride[0];
+  a.v_tile = pr.stride[1];
+  a.ks_tile = pr.stride[2];
+  a.vs_tile = pr.stride[3];
   a.map = TileMap{pool.table, pool.num_blocks, d.P, d.B, d.Hkv, d.cap / kChunk};
   a.r = r;
   a.b = b;
@@ -488,14 +558,8 @@ hx_status hx_pool_layout(const hx_kv_desc* desc, int32_t num_blocks, hx_kv_layou
   if (s) return s;
   if (num_blocks < 1) return fail(HX_EINVAL, "num_blocks=%d must be >= 1", num_blocks);
   const double tiles = (double)num_blocks * desc->Hkv;
-  if (tiles * (double)g.k_tile > 9.0e18) return fail(HX_EINVAL, "pool too large");
-  const int64_t t = (int64_t)num_blocks * desc->Hkv;
-  out->k_tile_bytes = (size_t)g.k_tile;
-  out->v_tile_bytes = (size_t)g.v_tile;
-  out->k_bytes = (size_t)(t * g.k_tile);
-  out->v_bytes = (size_t)(t * g.v_tile);
-  out->k_scale_bytes = (size_t)(t * g.ks_tile);
-  out->v_scale_bytes = (size_t)(t * g.vs_tile);
+  if (tiles * (double)(g.packed ? g.packed_tile : g.k_tile) > 9.0e18) return fail(HX_EINVAL, "pool too large");
+  plane_sizes(g, (int64_t)num_blocks * desc->Hkv, out);
   out->n_max = (int64_t)desc->P * desc->cap;
   return HX_OK;
 }
@@ -557,11 +621,10 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   s = check_heads(d, geo, Hq);
   if (s) return s;
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(HX_EINVAL, "scale must be finite and > 0");
-  if (!cache->k || (!d.v_alias_k && !cache->v)) return fail(HX_EINVAL, "null cache plane");
-  if (d.dtype != HX_KV_BF16 && (!cache->k_scale || (!d.v_alias_k && !cache->v_scale)))
-    return fail(HX_EINVAL, "null scale plane");
-  const void* ptrs[10] = {cache->k, cache->v, cache->k_scale, cache->v_scale, q, o_part, lse_part, ws,
-                          o_final, lse_final};
+  PlaneRefs pr;
+  s = plane_refs(d, geo, cache, &pr);
+  if (s) return s;
+  const void* ptrs[6] = {q, o_part, lse_part, ws, o_final, lse_final};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int G = Hq / d.Hkv;
@@ -578,10 +641,10 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
       return fail(HX_EINVAL, "ctx_len[%d]=%lld must be in [1, P*cap=%lld]", b, (long long)ctx_len[b], (long long)nmax);
 
   PartialArgs a{};
-  a.k = (const uint8_t*)cache->k;
-  a.v = (const uint8_t*)(d.v_alias_k ? cache->k : cache->v);
-  a.ks = (const uint8_t*)cache->k_scale;
-  a.vs = (const uint8_t*)(d.v_alias_k ? cache->k_scale : cache->v_scale);
+  a.k = pr.base[0];
+  a.v = pr.base[1];
+  a.ks = pr.base[2];
+  a.vs = pr.base[3];
   a.q = (const uint16_t*)q;
   a.o_part = o_part;
   a.lse_part = lse_part;
@@ -597,10 +660,10 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   a.cap_chunks = d.cap / kChunk;
   a.table = pool.table;
   a.num_blocks = pool.num_blocks;
-  a.k_tile = geo.k_tile;
-  a.v_tile = d.v_alias_k ? geo.k_tile : geo.v_tile;
-  a.ks_tile = geo.ks_tile;
-  a.vs_tile = d.v_alias_k ? geo.ks_tile : geo.vs_tile;
+  a.k_tile = pr.stride[0];
+  a.v_tile = pr.stride[1];
+  a.ks_tile = pr.stride[2];
+  a.vs_tile = pr.stride[3];
   a.c2 = scale * 1.44269504088896341f;
   a.split_p = (d.flags & HX_FLAG_P_BF16) == 0;
   const int64_t records = ws_records(d, geo.kind);

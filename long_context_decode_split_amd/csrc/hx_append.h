@@ -53,7 +53,7 @@ __device__ __forceinline__ void append_piece(const AppendArgs& a, int bl, int g,
   const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, lc);
   const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new;   // token-major source, this launch's rows
   const uint8_t* src = a.src[plane];
-  uint8_t* dst = a.dst[plane] + tile * a.tile_bytes[plane];
+  uint8_t* dst = a.dst[plane] + tile * a.tile_stride[plane];
 
   if (a.ebits[plane] == 32) {
     // one fp32 scale per chunk: taken from the first new token of the chunk
@@ -179,7 +179,7 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bl, int g, 
   const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new - pos;   // + token = source row
   for (int p = 0; p < a.nplanes; ++p) {
     const uint8_t* src = a.src[p];
-    uint8_t* dst = a.dst[p] + tile * a.tile_bytes[p];
+    uint8_t* dst = a.dst[p] + tile * a.tile_stride[p];
     const int64_t srow = a.src_row_bytes[p];
     const int eb = a.ebits[p], lay = a.lay[p], width = a.width[p];
     if (eb == 32) {   // the group's fp8 scale, from its first new token

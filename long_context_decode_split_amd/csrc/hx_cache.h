@@ -21,8 +21,8 @@ struct QAppendArgs {
   int64_t cap_chunks;
   const int32_t* table;    // pool cache block table (null: dense)
   int32_t num_blocks;
-  int64_t tile_bytes;      // code bytes per chunk tile
-  int64_t sc_tile_bytes;   // scale bytes per chunk tile
+  int64_t tile_stride;     // bytes between consecutive chunk tiles of a code plane
+  int64_t sc_tile_stride;  // bytes between consecutive chunk tiles of a scale plane
   int n_new;
   int max_chunks;
   int b0;
@@ -39,7 +39,7 @@ struct DequantArgs {
   float* k_out;
   float* v_out;
   int dtype, lay_k, lay_v, Dk, Dv, v_alias;
-  int64_t k_tile, v_tile, ks_tile, vs_tile;
+  int64_t k_tile, v_tile, ks_tile, vs_tile;   // bytes between consecutive tiles of each plane
   TileMap map;             // tile addressing of the cache
   int r, b, g;             // the slice rows read: slice r of request b, KV head g
   int64_t j0, n;

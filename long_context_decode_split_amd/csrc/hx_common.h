@@ -252,9 +252,14 @@ struct Geometry {
   int kind;            // 0 GQA (Dk = Dv = 128), 1 MLA (576 / 512, aliased, bf16)
   int lay_k, lay_v;    // tile layouts of the K and V code planes
   int ebits;           // bits per code element: 16, 8 or 4
-  int64_t k_tile, v_tile;          // bytes per chunk tile
-  int64_t ks_tile, vs_tile;        // bytes of scale per chunk tile (0 = none)
+  int64_t k_tile, v_tile;          // code bytes per chunk tile
+  int64_t ks_tile, vs_tile;        // scale bytes per chunk tile (0 = none)
   int64_t tiles;                   // P * B * Hkv * cap / 16
+  // MXFP4: the four parts of a chunk tile (K codes, V codes, K scales, V
+  // scales) are stored together, `packed_tile` bytes per tile in one plane,
+  // so a workgroup streams one contiguous run instead of four
+  bool packed;
+  int64_t packed_tile;
 };
 
 // Fills `g` from a validated descriptor; returns HX_EUNSUPPORTED for a
@@ -276,7 +281,8 @@ struct AppendArgs {
   int width[4];            // row width (row layouts)
   int ebits[4];            // element bits per plane (16, 8, 4; 32 = fp8 group scale)
   int64_t src_row_bytes[4];
-  int64_t tile_bytes[4];
+  int64_t tile_bytes[4];   // bytes of a chunk tile's part in this plane
+  int64_t tile_stride[4];  // bytes between consecutive chunk tiles of this plane
   int nplanes;
   int P, B, Hkv;
   int64_t cap_chunks;
@@ -303,7 +309,7 @@ struct PartialArgs {
   int64_t cap_chunks;
   const int32_t* table;    // block table of a pool cache (tile addressing above); null: dense
   int32_t num_blocks;
-  int64_t k_tile, v_tile, ks_tile, vs_tile;
+  int64_t k_tile, v_tile, ks_tile, vs_tile;   // bytes between consecutive tiles of each plane
   float c2;                // softmax scale * log2(e)
   int split_p;             // MLA: P as bf16 high part + residual (else rounded once)
   int fused_append;        // the workgroups first append app's rows into the tiles they own

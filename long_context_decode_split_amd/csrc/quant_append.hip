@@ -110,11 +110,11 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(const QAppendArg
   const int lay = a.lay[plane];
   // new row m of this tile is source token (row0 + m - pos) of this (request, head)
   const uint16_t* src = a.src[plane] + (((int64_t)bl * a.Hkv + g) * a.n_new + (row0 - pos)) * D;
-  uint8_t* tp = a.dst[plane] + tile * a.tile_bytes;
+  uint8_t* tp = a.dst[plane] + tile * a.tile_stride;
   const int tid = threadIdx.x;
 
   if (a.dtype == HX_KV_FP8_E4M3) {
-    float* scp = reinterpret_cast<float*>(a.sc[plane] + tile * a.sc_tile_bytes);
+    float* scp = reinterpret_cast<float*>(a.sc[plane] + tile * a.sc_tile_stride);
     // amax of the new rows, and whether a stored code of the group is non-zero
     float amax = 0.f, nz = 0.f;
     for (int i = tid; i < (m_hi - m_lo) * D; i += kThreads)
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(const QAppendArg
     if (touched) *reinterpret_cast<uint2*>(tp + byte0) = w;
     if (tid == 0) *scp = scale;
   } else {   // MXFP4: exponents per (new row, block), then codes
-    uint8_t* sp = a.sc[plane] + tile * a.sc_tile_bytes;
+    uint8_t* sp = a.sc[plane] + tile * a.sc_tile_stride;
     if (tid < kChunk * 4) {
       const int m = tid >> 2, j = tid & 3;
       if (m >= m_lo && m < m_hi) {

@@ -85,34 +85,53 @@ def test_layout_sizes(desc):
     lay = api.kv_layout(desc)
     tiles = desc.P * desc.B * desc.Hkv * desc.cap // 16
     bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
-    assert lay["k_tile_bytes"] == 16 * desc.Dk * bits // 8
+    codes = 16 * desc.Dk * bits // 8
+    assert lay["n_max"] == desc.P * desc.cap
+    if desc.dtype == "mxfp4":
+        # one plane: each tile holds K codes, V codes, K e8m0, V e8m0
+        assert lay["k_tile_bytes"] == 2 * codes + 2 * 16 * desc.Dk // 32 == 2176
+        assert lay["k_bytes"] == tiles * 2176
+        assert lay["v_bytes"] == lay["k_scale_bytes"] == lay["v_scale_bytes"] == lay["v_tile_bytes"] == 0
+        return
+    assert lay["k_tile_bytes"] == codes
     assert lay["k_bytes"] == tiles * lay["k_tile_bytes"]
     if desc.v_alias_k:
         assert lay["v_bytes"] == 0
     else:
         assert lay["v_bytes"] == tiles * 16 * desc.Dv * bits // 8
-    scale = {"bf16": 0, "fp8_e4m3": 4, "mxfp4": 16 * desc.Dk // 32}[desc.dtype]
+    scale = {"bf16": 0, "fp8_e4m3": 4}[desc.dtype]
     assert lay["k_scale_bytes"] == tiles * scale
-    assert lay["n_max"] == desc.P * desc.cap
 
 
 @pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.dtype}-{d.Dk}")
 def test_tile_layout_is_a_bijection(desc):
+    """Every code element of K and V (and every MXFP4 scale byte of a packed
+    tile) has its own place, and together they fill the tile exactly."""
     lay = api.kv_layout(desc)
-    for which, width, tile in ((0, desc.Dk, lay["k_tile_bytes"]), (1, desc.Dv, lay["v_tile_bytes"])):
+    bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
+    unit = {16: 4, 8: 2, 4: 1}[bits]            # off2 units per element
+    packed = desc.dtype == "mxfp4"
+    for which, width in ((0, desc.Dk), (1, desc.Dv)):
         if which == 1 and desc.v_alias_k:
             continue
-        bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
         offs = set()
         for m in range(16):
             for d in range(width):
                 o2 = api.kv_tile_offset(desc, which, m, d)
-                if bits == 16:
-                    assert o2 % 4 == 0
-                elif bits == 8:
-                    assert o2 % 2 == 0
-                offs.add(o2 // {16: 4, 8: 2, 4: 1}[bits])
-        assert offs == set(range(tile * 8 // bits)), "elements must fill the tile exactly once"
+                assert o2 % unit == 0
+                offs.add(o2 // unit)
+        codes = 16 * width * bits // 8
+        lo = codes * 8 // bits if packed and which == 1 else 0    # packed: V codes follow K codes
+        assert offs == set(range(lo, lo + codes * 8 // bits)), "elements must fill their part of the tile once"
+    if packed:
+        scale_bytes = set()
+        for which in (2, 3):
+            for m in range(16):
+                for d in range(0, desc.Dk, 32):
+                    o2 = api.kv_tile_offset(desc, which, m, d)
+                    assert o2 % 2 == 0 and api.kv_tile_offset(desc, which, m, d + 31) == o2
+                    scale_bytes.add(o2 // 2)
+        assert scale_bytes == set(range(2048, lay["k_tile_bytes"])), "K then V e8m0 bytes end the tile"
 
 
 def test_gqa_bf16_tile_gives_lane_fragments():
@@ -130,7 +149,12 @@ def test_tile_offset_errors():
     with pytest.raises(api.HXError):
         api.kv_tile_offset(DESCS[0], 0, 16, 0)
     with pytest.raises(api.HXError):
-        api.kv_tile_offset(DESCS[0], 2, 0, 0)
+        api.kv_tile_offset(DESCS[0], 2, 0, 0)          # bf16: no scales
+    with pytest.raises(api.HXError):
+        api.kv_tile_offset(DESCS[2], 4, 0, 0)
+    with pytest.raises(api.HXError):
+        api.kv_tile_offset(DESCS[3], 1, 0, 0)          # MLA: V aliases K
+    assert api.kv_tile_offset(DESCS[1], 3, 5, 77) == 0  # fp8: the tile's one float
 
 
 @pytest.mark.parametrize("bad,status", [

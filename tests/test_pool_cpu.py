@@ -28,11 +28,14 @@ def _blocks(n, P):
 
 
 def test_pool_layout_sizes():
-    for dtype, kt, st in (("bf16", 4096, 0), ("fp8_e4m3", 2048, 4), ("mxfp4", 1024, 64)):
+    for dtype, kt, st in (("bf16", 4096, 0), ("fp8_e4m3", 2048, 4)):
         lay = api.pool_layout(_desc(dtype=dtype), 37)
         assert lay["k_tile_bytes"] == kt and lay["k_bytes"] == 37 * 2 * kt and lay["v_bytes"] == 37 * 2 * kt
         assert lay["k_scale_bytes"] == 37 * 2 * st and lay["v_scale_bytes"] == 37 * 2 * st
         assert lay["n_max"] == 4 * 256
+    lay = api.pool_layout(_desc(dtype="mxfp4"), 37)       # packed tiles: one plane
+    assert lay["k_tile_bytes"] == 2176 and lay["k_bytes"] == 37 * 2 * 2176
+    assert lay["v_bytes"] == lay["k_scale_bytes"] == lay["v_scale_bytes"] == 0
     mla = api.KVDesc(P=8, B=1, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="bf16", cap=64)
     lay = api.pool_layout(mla, 5)
     assert lay["k_bytes"] == 5 * 16 * 1152 and lay["v_bytes"] == 0
