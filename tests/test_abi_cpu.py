@@ -312,3 +312,37 @@ def test_dequant_and_combine_argument_checks():
     assert L.hx_lse_combine(0, 1, 1, 1, _fake(16), _fake(32), _fake(48), _fake(64), None) == _lib.HX_EINVAL
     assert L.hx_lse_combine(2, 1, 1, 1, _fake(16), _fake(33), _fake(48), _fake(64), None) == _lib.HX_EINVAL
     assert L.hx_lse_combine(2, 1, 1, 1, None, _fake(32), _fake(48), _fake(64), None) == _lib.HX_EINVAL
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "helixdecode.h"
+
+int main(void) {
+  int32_t r; int64_t j, len;
+  hx_kv_desc d = {8, 2, 1, 128, 128, 0, HX_KV_MXFP4, 0, 1024};
+  hx_kv_layout_info lay;
+  if (hx_slot(40, 2, &r, &j) != HX_OK) return 1;
+  if (hx_slice_len(4137, 8, 2, &len) != HX_OK) return 2;
+  if (hx_kv_layout(&d, &lay) != HX_OK) return 3;
+  if (hx_slot(-1, 2, &r, &j) != HX_EINVAL || hx_last_error()[0] == 0) return 4;
+  printf("%d %lld %lld %zu %zu\n", r, (long long)j, (long long)len, lay.k_bytes, lay.v_bytes);
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c(tmp_path):
+    """A C99 program includes the header, links the library and calls its
+    host-only entry points: the boundary needs no C++ and no torch."""
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe),
+           f"-L{libdir}", "-lhelixdecode", f"-Wl,-rpath,{libdir}"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout.split()
+    # token 40 with P = 2: group 2 -> slice 0, local row 16 + 8; slice 2 of a 4137-token request (P = 8): 521 rows
+    assert out[:3] == ["0", "24", str(placement.slice_len(4137, 8, 2))]
+    assert int(out[3]) == 8 * 2 * 1 * (1024 // 16) * 2176 and out[4] == "0"
