@@ -121,10 +121,12 @@ def recorded_traffic(w, layout="dense"):
     return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
-def cpu_baseline(inp, budget_s=20.0):
+def cpu_baseline(inp, budget_s=20.0, o=None, lse=None):
     """The oracle (fp64, numpy) on a bounded sample of the same step: whole
     (request, KV head) groups over their full context, as many as fit the
-    time budget (at least one); scaled to KV-read GB/s like the GPU value."""
+    time budget (at least one); scaled to KV-read GB/s like the GPU value.
+    With the step's final outputs `o`, `lse` (device tensors) it also
+    returns their largest deviations from the oracle over those groups."""
     from oracle import attention as oatt
     from oracle import codecs as ocod
 
@@ -132,6 +134,9 @@ def cpu_baseline(inp, budget_s=20.0):
     G = w.G
     per_tok = roofline.kv_bytes_per_token(w.Dk, w.Dv, w.v_alias_k, w.dtype)
     done_bytes, t_total, groups = 0.0, 0.0, 0
+    err_o = err_l = 0.0
+    oc = None if o is None else o.float().cpu().numpy()
+    lc = None if lse is None else lse.float().cpu().numpy()
     order = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     for b, g in order:
         n = inp.ctx[b]
@@ -151,15 +156,22 @@ def cpu_baseline(inp, budget_s=20.0):
         else:
             K = ocod.dequant_mxfp4(kc.numpy(), ks)
             V = K[:, :w.Dv] if w.v_alias_k else ocod.dequant_mxfp4(vc.numpy(), vs)
-        oatt.attend(q, K, V, w.softmax_scale)
+        O, L = oatt.attend(q, K, V, w.softmax_scale)
         t_total += time.perf_counter() - t0
+        if oc is not None:
+            err_o = max(err_o, float(np.max(np.abs(oc[b, g * G:(g + 1) * G] - O))))
+            err_l = max(err_l, float(np.max(np.abs(lc[b, g * G:(g + 1) * G] - L) / np.maximum(1.0, np.abs(L)))))
         done_bytes += n * per_tok
         groups += 1
         del K, V
         if t_total >= budget_s:
             break
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {
+    parity = None if oc is None else {
+        "groups": groups, "max_abs_dO": err_o, "max_rel_dLSE": err_l,
+        "bound_abs_dO": 2e-3 if w.dtype == "bf16" else 2e-2, "bound_rel_dLSE": 1e-4,
+        "reference": "the oracle on the same stored K/V (dequantised values for fp8 / MXFP4)"}
+    return parity, {
         "value": done_bytes / t_total / 1e9,
         "unit": "GB/s",
         "cores": threads,
@@ -317,10 +329,11 @@ def main():
     log(f"[bench] step {step_ms * 1e3:.1f} us, partial kernel {kern_avg_ms * 1e3:.1f} us "
         f"(min {min(kern_ms) * 1e3:.1f}, max {max(kern_ms) * 1e3:.1f}), {kern_gbs:.0f} GB/s")
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_budget)
-        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+        parity, cpu = cpu_baseline(inp, args.cpu_budget, o, lse)
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']}); "
+            f"max |dO| {parity['max_abs_dO']:.2e}, LSE rel {parity['max_rel_dLSE']:.2e}")
 
     out = {
         "metric": METRIC,
@@ -363,6 +376,7 @@ def main():
             "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 2),
         },
         "cpu_baseline": cpu,
+        "parity": parity,
         "timing_us": {"step": pct(step_each_ms), "partial": pct(kern_ms),
                       "cache": "flushed before every step" if flush is not None else "hot (back-to-back steps)"},
     }
