@@ -262,7 +262,8 @@ def decode_attn_partial(cache: KVCache, q, ctx_len, scale, o_part, lse_part, ws,
 
 def decode_attn(cache: KVCache, q, ctx_len, scale, o, lse, ws, stream=None):
     """``hx_decode_attn``: q bf16 [B, Hq, Dk] -> o f32 [B, Hq, Dv], lse f32
-    [B, Hq] (the whole step; ws zeroed once before its first use here)."""
+    [B, Hq] (the whole step).  ``ws`` is scratch of ``workspace_size`` bytes;
+    it needs no initialisation."""
     Hq = q.shape[1]
     check(lib().hx_decode_attn(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq, _i64(ctx_len),
                                float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),

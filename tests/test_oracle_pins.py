@@ -182,6 +182,30 @@ def test_round_robin_slices_combine_to_unsplit(n, P):
     assert np.max(np.abs(Oc - O)) <= 1e-12 and np.max(np.abs(Lc - L)) <= 1e-12
 
 
+def check_slice_partials(partials_fn):
+    """Slice r's partial is the unsplit attention over exactly the tokens the
+    placement enumerates for slice r (a slipped slice index or a wrong mask
+    fails here even though the combine of all slices would not notice)."""
+    rng = np.random.default_rng(99)
+    for n, P in [(1, 3), (17, 2), (100, 3), (257, 4), (600, 8), (40, 8)]:
+        q = rng.normal(size=(3, 8))
+        K = rng.normal(size=(n, 8))
+        V = rng.normal(size=(n, 6))
+        Op, Lp = partials_fn(q, K, V, 0.3, P)
+        for r in range(P):
+            toks = placement.slice_tokens(n, P, r)
+            O, L = attention.attend(q, K[toks], V[toks], 0.3)
+            if not toks:
+                assert np.all(Op[r] == 0) and np.all(np.isneginf(Lp[r])), (n, P, r)
+                continue
+            assert np.max(np.abs(Op[r] - O)) <= 1e-12, (n, P, r)
+            assert np.max(np.abs(Lp[r] - L)) <= 1e-12 * max(1, np.max(np.abs(L))), (n, P, r)
+
+
+def test_slice_partials_follow_the_placement():
+    check_slice_partials(attention.slice_partials)
+
+
 def test_slice_mask_matches_enumeration():
     for P in (1, 2, 3, 8):
         for n in (0, 1, 16, 17, 100, 257):
@@ -407,6 +431,27 @@ def test_mutant_combine_is_caught(mutant):
     with pytest.raises(AssertionError):
         for seed in range(5):
             check_split_invariance(attention.attend, mutant, seed, 50, 4)
+
+
+def _partials_slice_slip(q, K, V, scale, P):
+    Op, Lp = attention.slice_partials(q, K, V, scale, P)
+    return np.roll(Op, 1, axis=0), np.roll(Lp, 1, axis=0)
+
+
+def _partials_blockwise_mask(q, K, V, scale, P):
+    n = K.shape[0]
+    O = np.empty((P, q.shape[0], V.shape[1]))
+    L = np.empty((P, q.shape[0]))
+    for r in range(P):      # contiguous blocks instead of the 16-token rotation
+        idx = np.arange(n)[(np.arange(n) * P) // max(n, 1) == r]
+        O[r], L[r] = attention.attend(q, K[idx], V[idx], scale)
+    return O, L
+
+
+@pytest.mark.parametrize("mutant", [_partials_slice_slip, _partials_blockwise_mask])
+def test_mutant_slice_partials_is_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_slice_partials(mutant)
 
 
 @pytest.mark.parametrize("mutant", [_slot_blockwise, _slot_one_based])
