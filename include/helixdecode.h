@@ -165,10 +165,14 @@ hx_status hx_kv_tile_offset(const hx_kv_desc* desc, int32_t which, int32_t m, in
  *   v_alias_k): bf16 -> 2 bytes per element; fp8 -> 1 byte; MXFP4 -> packed
  *   bytes [..][Dk/2], even element in the low nibble;
  *   k_scale_new / v_scale_new: fp8 -> float [B][Hkv][n_new], the scale of
- *   the 16-token group each token falls in (the group's stored scale is
- *   taken from the first new token of that group in this call; every token
- *   of a group must carry the same scale, since earlier codes of a group
- *   keep the stored scale); MXFP4 -> uint8 e8m0 [B][Hkv][n_new][D/32];
+ *   the 16-token group each token falls in.  A group whose first row is
+ *   among the new tokens takes the scale of that row; a group that already
+ *   holds rows keeps its stored scale, and new codes of such a group are
+ *   read under it (the scales of its new tokens are not used), so they must
+ *   have been made with that scale.  The scales are device data the host
+ *   does not see, so a mismatch cannot be reported; hx_kv_append_bf16 and
+ *   hx_decode_step_bf16 quantise on the device and keep each group's scale
+ *   consistent by themselves.  MXFP4 -> uint8 e8m0 [B][Hkv][n_new][D/32];
  *   bf16 -> NULL.
  * Pure placement: the bytes are copied, never converted, so it is
  * bit-exact.  Rows outside [pos[b], pos[b] + count[b]) are left unchanged.
@@ -363,9 +367,11 @@ hx_status hx_block_pool_free_count(const hx_block_pool* pool, int32_t* n_free);
 
 /* Make request b's lists cover a context of n tokens: every entry (b, r, c)
  * with c < ceil(hx_slice_len(n, P, r) / 16) that holds -1 gets a free block;
- * entries already holding a block keep it (each must be a block handed to
- * request b, else HX_EINVAL).  All or nothing: with too few free blocks
- * nothing changes and HX_ENOSPC is returned.  *n_taken (may be NULL)
+ * entries already holding a block keep it.  Every entry of request b's
+ * lists other than -1 must be a block handed to request b, and no block may
+ * be listed twice (else HX_EINVAL, as for hx_block_pool_release).  All or
+ * nothing: on any error nothing changes; with too few free blocks
+ * HX_ENOSPC is returned.  *n_taken (may be NULL)
  * receives the number of blocks handed out.  0 <= n <= P * cap. */
 hx_status hx_block_pool_reserve(hx_block_pool* pool, const hx_kv_desc* desc, int32_t* table_host, int32_t b,
                                 int64_t n, int32_t* n_taken);

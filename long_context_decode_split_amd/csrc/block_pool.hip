@@ -17,6 +17,8 @@ struct hx_block_pool {
   int32_t n = 0;
   std::vector<int32_t> free_ids;   // stack: back() is handed out next
   std::vector<int32_t> owner;      // request + 1 holding the block, 0 when free
+  std::vector<uint32_t> seen;      // duplicate check: seen[id] == epoch once id was met in this scan
+  uint32_t epoch = 0;
 };
 
 namespace hx {
@@ -33,6 +35,29 @@ hx_status check_table_args(const hx_block_pool* pool, const hx_kv_desc* desc, co
 
 // Whether `id` is a block of this pool handed to request b.
 bool held_by(const hx_block_pool& p, int32_t id, int32_t b) { return id >= 0 && id < p.n && p.owner[id] == b + 1; }
+
+// Every entry of request b's lists (rows, m entries) other than -1 must be a
+// block handed to request b, listed once.  O(m), no allocation: a block is
+// marked with the scan's epoch when first met.  Appends the ids to `ids`
+// when given.  Caller holds the pool's lock.
+hx_status check_request_entries(hx_block_pool& p, const int32_t* rows, int64_t m, int32_t b,
+                                std::vector<int32_t>* ids) {
+  if (++p.epoch == 0) {   // wrapped: clear the marks once every 2^32 scans
+    std::fill(p.seen.begin(), p.seen.end(), 0u);
+    p.epoch = 1;
+  }
+  for (int64_t i = 0; i < m; ++i) {
+    const int32_t id = rows[i];
+    if (id == -1) continue;
+    if (!held_by(p, id, b))
+      return fail(HX_EINVAL, "table entry %lld of request %d = %d is not a block of this pool held by it", (long long)i,
+                  b, id);
+    if (p.seen[id] == p.epoch) return fail(HX_EINVAL, "request %d lists block %d twice", b, id);
+    p.seen[id] = p.epoch;
+    if (ids) ids->push_back(id);
+  }
+  return HX_OK;
+}
 
 }  // namespace
 }  // namespace hx
@@ -53,6 +78,7 @@ hx_status hx_block_pool_create(int32_t num_blocks, hx_block_pool** out) {
     p->free_ids.resize(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) p->free_ids[i] = num_blocks - 1 - i;   // 0 first
     p->owner.assign(num_blocks, 0);
+    p->seen.assign(num_blocks, 0u);
   } catch (...) {
     delete p;
     return fail(HX_ENOSPC, "out of host memory");
@@ -81,17 +107,16 @@ hx_status hx_block_pool_reserve(hx_block_pool* pool, const hx_kv_desc* desc, int
     return fail(HX_EINVAL, "n=%lld must be in [0, P*cap=%lld]", (long long)n, (long long)d.P * d.cap);
   const int64_t capc = d.cap / kChunk;
   std::lock_guard<std::mutex> lk(pool->mu);
+  // the request's lists as they stand must be valid (as hx_block_pool_release
+  // requires): blocks of this request, none listed twice
+  s = check_request_entries(*pool, table_host + (int64_t)b * d.P * capc, (int64_t)d.P * capc, b, nullptr);
+  if (s) return s;
   int64_t need = 0;
   for (int r = 0; r < d.P; ++r) {
     const int32_t* row = table_host + ((int64_t)b * d.P + r) * capc;
     const int64_t groups = (slice_len(n, d.P, r) + kChunk - 1) / kChunk;
-    for (int64_t c = 0; c < groups; ++c) {
-      if (row[c] == -1)
-        ++need;
-      else if (!held_by(*pool, row[c], b))
-        return fail(HX_EINVAL, "table entry (b=%d, r=%d, c=%lld) = %d is not a block of this pool held by request %d",
-                    b, r, (long long)c, row[c], b);
-    }
+    for (int64_t c = 0; c < groups; ++c)
+      if (row[c] == -1) ++need;
   }
   if (need > (int64_t)pool->free_ids.size())
     return fail(HX_ENOSPC, "request %d needs %lld more blocks, %zu free", b, (long long)need, pool->free_ids.size());
@@ -121,17 +146,8 @@ hx_status hx_block_pool_release(hx_block_pool* pool, const hx_kv_desc* desc, int
   std::lock_guard<std::mutex> lk(pool->mu);
   // check every entry first
   std::vector<int32_t> ids;
-  for (int64_t i = 0; i < m; ++i) {
-    if (rows[i] == -1) continue;
-    if (!held_by(*pool, rows[i], b))
-      return fail(HX_EINVAL, "table entry %lld of request %d = %d is not a block of this pool held by it", (long long)i,
-                  b, rows[i]);
-    ids.push_back(rows[i]);
-  }
-  std::vector<int32_t> sorted(ids);
-  std::sort(sorted.begin(), sorted.end());
-  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
-    return fail(HX_EINVAL, "request %d lists a block twice", b);
+  s = check_request_entries(*pool, rows, m, b, &ids);
+  if (s) return s;
   // free in reverse list order, so the request's first block is handed out first again
   for (auto it = ids.rbegin(); it != ids.rend(); ++it) {
     pool->owner[*it] = 0;

@@ -248,6 +248,15 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
 #pragma unroll
   for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
 
+  // fp8: the tile's K scale is applied to the scores before the max and the
+  // masking, so a zero scale (scores 0) or a negative one (order reversed)
+  // still gives the right max, and masked rows stay at exactly -inf (a
+  // masked -inf times a zero scale would be NaN).  The other formats scale
+  // by c2 > 0 inside the exponent.
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] *= cscale;
+  }
   uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;   // V halves of tokens 4h+{0,1} / 4h+{2,3}
   if constexpr (TAIL) {
 #pragma unroll
@@ -264,7 +273,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   // more than kHeadroom: P = 2^(s - mrun) is bounded by 2^kHeadroom, and the
   // rescale of the accumulator (32 multiplies; a factor of exactly 1 for the
   // heads whose max did not move) runs only on the tiles that raise it.
-  const float cms = cm * cscale;
+  const float cms = FMT == 1 ? cm : cm * cscale;
   if (__any(cms > st.mrun + kHeadroom<FMT>)) {   // wave-uniform
     const float mnew = fmaxf(st.mrun, cms);
     const float alpha = __builtin_amdgcn_exp2f(st.mrun - mnew);
@@ -276,7 +285,8 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
   float p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], cscale, -st.mrun));
+  for (int i = 0; i < 4; ++i)
+    p[i] = __builtin_amdgcn_exp2f(FMT == 1 ? sc[i] - st.mrun : fmaf(sc[i], cscale, -st.mrun));
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
 
   // ---- P^T fragments (bf16) and V^T fragments, then O^T += V^T P^T
@@ -305,10 +315,12 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
     for (int i = 0; i < 8; ++i) st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[i], pl, st.acc[i], 0, 0, 0);
   } else if constexpr (FMT == 1) {
     // The tile's V scale is folded into P; the rounded products, divided by
-    // the scale, are what normalises O.
+    // the scale, are what normalises O.  A zero V scale makes the tile's
+    // values exactly 0: its weights then enter the normalisation unrounded.
     const float vsc = cur.vs;
     const uint32_t p01 = pack_bf16(p[0] * vsc, p[1] * vsc), p23 = pack_bf16(p[2] * vsc, p[3] * vsc);
-    st.lsum_mfma = fmaf(add_bf16x2(p23, add_bf16x2(p01, 0.f)), __builtin_amdgcn_rcpf(vsc), st.lsum_mfma);
+    const float rounded = add_bf16x2(p23, add_bf16x2(p01, 0.f));
+    st.lsum_mfma += vsc != 0.f ? rounded * __builtin_amdgcn_rcpf(vsc) : (p[0] + p[1]) + (p[2] + p[3]);
     const s16x4 pb = as_s16x4(p01, p23);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {

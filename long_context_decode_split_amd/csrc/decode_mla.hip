@@ -79,13 +79,19 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // the compiler does not treat the address registers as pending load results
 // (it would otherwise wait for the tile loads before every reuse of those
 // registers).  Completion is awaited with explicit vmcnt waits before the
-// barrier that publishes a tile; no other M0 user is live in the kernel.
+// barrier that publishes a tile.  M0 is an input operand of the asm (the
+// "{m0}" constraint), so the compiler itself sets it and knows it is used.
+// The compiler cannot see the load inside the asm, so the asm carries the
+// wait states it needs: five after a VALU write of an SGPR the load reads
+// (the readfirstlanes of the base address; the compiler pads the same
+// sequence with s_nop 4 when it emits the load itself), which also covers
+// the one wait state after the M0 write.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
   const uint64_t sb = (uint64_t)sbase;
   const uint64_t sbu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbu),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbu),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 

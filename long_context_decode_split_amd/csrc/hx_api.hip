@@ -607,10 +607,12 @@ namespace hx {
 // slice's partial or split records straight into the final output.
 // With `fuse` (an append_setup result) and its host positions, the partial
 // kernels first append those rows into the tiles they own (hx_decode_step).
+// With `check_only`, every argument is checked and nothing is launched.
 static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* q,
                              int32_t Hq, const int64_t* ctx_len, float scale, float* o_part, float* lse_part,
                              void* ws, size_t ws_bytes, void* stream, float* o_final, float* lse_final,
-                             const AppendArgs* fuse = nullptr, const int64_t* fuse_pos = nullptr) {
+                             const AppendArgs* fuse = nullptr, const int64_t* fuse_pos = nullptr,
+                             bool check_only = false) {
   const bool final_out = o_final != nullptr;
   if (!desc || !cache || !q || !ctx_len || !ws) return fail(HX_EINVAL, "null argument");
   if (final_out ? !lse_final : (!o_part || !lse_part)) return fail(HX_EINVAL, "null argument");
@@ -639,6 +641,7 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   for (int b = 0; b < d.B; ++b)
     if (ctx_len[b] < 1 || ctx_len[b] > nmax)
       return fail(HX_EINVAL, "ctx_len[%d]=%lld must be in [1, P*cap=%lld]", b, (long long)ctx_len[b], (long long)nmax);
+  if (check_only) return HX_OK;
 
   PartialArgs a{};
   a.k = pr.base[0];
@@ -787,6 +790,11 @@ static hx_status fused_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
                              &base);
   if (s) return s;
   if (desc->dtype == HX_KV_MXFP4) {   // no fused kernel for MXFP4 (see decode_gqa.hip): append, then attend
+    // every argument of the attention is checked before the append writes the
+    // cache, so a call that fails leaves the cache unchanged
+    s = decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse, nullptr,
+                    nullptr, true);
+    if (s) return s;
     s = kv_append(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos.data(), nullptr, n_new, stream);
     if (s) return s;
     return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);

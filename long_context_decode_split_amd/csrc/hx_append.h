@@ -56,9 +56,10 @@ __device__ __forceinline__ void append_piece(const AppendArgs& a, int bl, int g,
   uint8_t* dst = a.dst[plane] + tile * a.tile_stride[plane];
 
   if (a.ebits[plane] == 32) {
-    // one fp32 scale per chunk: taken from the first new token of the chunk
-    const int64_t tf = row0 > pos ? row0 : pos;
-    const float v = reinterpret_cast<const float*>(src)[src_tok0 + (tf - pos)];
+    // one fp32 scale per chunk: a chunk whose first row is new takes the scale
+    // of that row; a chunk that already holds rows keeps its stored scale
+    if (row0 < pos) return;
+    const float v = reinterpret_cast<const float*>(src)[src_tok0 + (row0 - pos)];
     *reinterpret_cast<float*>(dst) = v;
     return;
   }
@@ -182,8 +183,8 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bl, int g, 
     uint8_t* dst = a.dst[p] + tile * a.tile_stride[p];
     const int64_t srow = a.src_row_bytes[p];
     const int eb = a.ebits[p], lay = a.lay[p], width = a.width[p];
-    if (eb == 32) {   // the group's fp8 scale, from its first new token
-      if (tid == 0) *reinterpret_cast<float*>(dst) = reinterpret_cast<const float*>(src)[src_tok0 + row0 + mlo];
+    if (eb == 32) {   // the group's fp8 scale: set when its first row is new, else kept
+      if (tid == 0 && mlo == 0) *reinterpret_cast<float*>(dst) = reinterpret_cast<const float*>(src)[src_tok0 + row0];
       continue;
     }
     if (eb == 16 || eb == 8) {

@@ -31,6 +31,10 @@ CASES = [
     (configs.TINY_GQA.scaled(B=66, Hkv=1, Hq=4, ctx=None, ctx_range=(20, 300), P=2), 1, "dense"),  # two launches
     (configs.MXFP4_RAGGED.scaled(B=2, ctx_range=(40, 9000), P=4), 1, "paged"),
     (configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(40, 3000), P=4), 1, "paged"),
+    (configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(20000, 60000)), 1, "paged"),   # bf16, split slices
+    (configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(40, 9000)), 17, "paged"),
+    (configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(40, 9000)), 1, "paged"),
+    (configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(40, 9000)), 17, "paged"),
 ]
 
 
@@ -91,3 +95,29 @@ def test_fused_step_equals_append_then_attend(w, n_new, layout):
         _, _, O, L = H.oracle_group(inp, b, g, heads)
         cols = g * w.G + heads
         H.compare(f"decode step b={b} g={g}", oc[b, cols], lc[b, cols], O, L, w.dtype)
+
+
+def test_failed_mxfp4_step_leaves_the_cache_unchanged():
+    """hx_decode_step on an MXFP4 cache appends with a separate kernel before
+    the attention; every argument of the attention is checked first, so a
+    call refused for a too-small workspace writes nothing."""
+    w = configs.MXFP4_RAGGED.scaled(B=2, ctx_range=(40, 3000), P=4)
+    inp = synth.make_inputs(w, 31, device=DEV)
+    desc = H.desc_of(inp)
+    before = [n - 1 for n in inp.ctx]
+    c = api.KVCache(desc, device=DEV, fill=0xFF)
+    api.kv_append(c, inp.k, inp.v, inp.k_scale, inp.v_scale, pos=[0] * w.B, count=before)
+    torch.cuda.synchronize()
+    snap = [t.clone() for t in _planes(c)]
+    new = [_newest(t, inp.ctx, 1) for t in (inp.k, inp.v, inp.k_scale, inp.v_scale)]
+    ws = torch.zeros(api.workspace_size(desc, w.Hq) - 256, dtype=torch.uint8, device=DEV)
+    o = torch.empty(w.B, w.Hq, w.Dv, device=DEV)
+    lse = torch.empty(w.B, w.Hq, device=DEV)
+    with pytest.raises(api.HXError) as e:
+        api.decode_step(c, *new, inp.q, inp.ctx, w.softmax_scale, o, lse, ws)
+    assert e.value.status == 1 and "workspace" in str(e.value)
+    with pytest.raises(api.HXError):      # and a bad scale
+        api.decode_step(c, *new, inp.q, inp.ctx, float("nan"), o, lse, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(snap, _planes(c)):
+        assert torch.equal(a, b), "a refused step wrote the cache"

@@ -192,6 +192,62 @@ def test_mxfp4_every_code_and_exponent_dequantises_exactly():
     _check_placement(inp, cache)
 
 
+def test_fp8_open_group_keeps_its_stored_scale():
+    """Storage-format append into an fp8 group that already holds rows: the
+    group keeps its stored scale (the new tokens' scales are not used), so
+    the earlier rows decode as before; a group whose first row is new takes
+    the scale of that row."""
+    w = configs.FP8_GQA.scaled(B=1, Hkv=1, Hq=4, ctx=None, ctx_range=(40, 40), P=2)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    codes = torch.randint(0, 0x7F, (1, 1, 40, w.Dk), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    vcodes = torch.randint(0, 0x7F, (1, 1, 40, w.Dv), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    s1 = torch.full((1, 1, 40), 0.5, device=DEV)
+    s2 = torch.full((1, 1, 40), 3.0, device=DEV)
+    inp = synth.Inputs(w=w, seed=0, ctx=[40], cap=synth.capacity([40], w.P), q=torch.zeros(1, 4, w.Dk, dtype=torch.bfloat16,
+                                                                                            device=DEV),
+                       k=codes, v=vcodes, k_scale=s1, v_scale=s1)
+    cache = H.build_cache(inp, upto=[5])                                  # rows 0-4 of group 0 with scale 0.5
+    tail = lambda t: t[:, :, 5:].clone()                  # source row i is token 5 + i (fresh, aligned)
+    api.kv_append(cache, tail(codes), tail(vcodes), tail(s2), tail(s2), pos=[5], count=[30])   # tokens 5-34
+    torch.cuda.synchronize()
+    ko = torch.empty(24, w.Dk, device=DEV)
+    vo = torch.empty(24, w.Dv, device=DEV)
+    api.kv_dequant(cache, 0, 0, 0, 0, 24, ko, vo)          # slice 0: group 0 (rows 0-15), group 2 (rows 16-23 = tokens 32-39)
+    expect_k = ocod.dequant_fp8(codes[0, 0].cpu().numpy(), np.array([0.5, 0.5, 3.0], dtype=np.float32))
+    expect_v = ocod.dequant_fp8(vcodes[0, 0].cpu().numpy(), np.array([0.5, 0.5, 3.0], dtype=np.float32))
+    rows = opl.slice_tokens(35, w.P, 0)                     # tokens held by slice 0 after 35 tokens
+    assert _same_f32(ko[:len(rows)].cpu().numpy(), expect_k[rows].astype(np.float32))
+    assert _same_f32(vo[:len(rows)].cpu().numpy(), expect_v[rows].astype(np.float32))
+    ko1 = torch.empty(16, w.Dk, device=DEV)
+    api.kv_dequant(cache, 1, 0, 0, 0, 16, ko1, None)       # slice 1: group 1 (tokens 16-31), first row new: scale 3
+    torch.cuda.synchronize()
+    expect_k1 = ocod.dequant_fp8(codes[0, 0, 16:32].cpu().numpy(), np.array([3.0], dtype=np.float32))
+    assert _same_f32(ko1.cpu().numpy(), expect_k1.astype(np.float32))
+
+
+def test_fp8_zero_scales_in_the_last_tile():
+    """A zero K or V scale is a valid encoding (all values 0).  In the last,
+    partial tile of a slice the masked rows must not turn it into NaN: the
+    scores of a zero-K-scale group are 0, and a zero-V-scale group adds
+    weight but no value."""
+    w = configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(1000, 3000), P=4)
+    inp = synth.make_inputs(w, 61, device=DEV, needles=True)
+    for b, n in enumerate(inp.ctx):
+        last = (n - 1) // 16 * 16                          # first token of the last (partial) group
+        if b in (0, 2):
+            inp.k_scale[b, :, last:n] = 0.0
+        if b in (1, 2):
+            inp.v_scale[b, :, last:n] = 0.0
+        inp.k_scale[b, :, 160:176] = 0.0                   # and one full group inside a slice
+    H.log(f"[fp8 zero scales] ctx={inp.ctx}")
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label="fp8 zero scales")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
 # ---------------------------------------------------------------- attention parity
 
 PARITY_CASES = [

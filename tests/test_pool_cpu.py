@@ -113,6 +113,32 @@ def test_release_rejects_foreign_or_duplicate_entries():
     assert pool.free_blocks() == 10
 
 
+def test_reserve_rejects_a_block_listed_twice():
+    """A request's own block listed under two of its entries: reserve refuses
+    it (as release does), leaving the pool and the table unchanged, whether
+    the duplicate lies inside the rows being covered or beyond them."""
+    d = _desc(P=2, B=2, cap=128)
+    pool = api.KVPool(d, 20, device="cpu")
+    pool.reserve(0, 40)
+    snap = pool.table_host.copy()
+    free = pool.free_blocks()
+    own = int(snap[0, 0, 0])
+    for r, c in ((1, 1), (0, 6)):               # (1, 1) is needed for 100 tokens, (0, 6) is not
+        pool.table_host[...] = snap
+        pool.table_host[0, r, c] = own
+        before = pool.table_host.copy()
+        with pytest.raises(HXError) as e:
+            pool.reserve(0, 100)
+        assert e.value.status == HX_EINVAL and "twice" in str(e.value)
+        assert np.array_equal(before, pool.table_host) and pool.free_blocks() == free
+        with pytest.raises(HXError):
+            pool.release(0)
+    pool.table_host[...] = snap
+    assert pool.reserve(0, 100) == _blocks(100, 2) - _blocks(40, 2)
+    pool.release(0)
+    assert pool.free_blocks() == 20
+
+
 def test_allocator_argument_errors():
     L = lib()
     h = ctypes.c_void_p()
