@@ -257,6 +257,21 @@ hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const
                          const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* hx_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, kernels and
+ * results as hx_decode_attn (bit for bit); the scratch is the library's own
+ * fixed array of 128 MiB per device (allocated when the library's code is
+ * loaded on that device and held until the process ends), so the call
+ * allocates nothing.  A call whose split records and slice partials need
+ * more than 128 MiB returns HX_EINVAL (then use hx_decode_attn); every
+ * workload up to 8 requests x 128 MLA heads x 2^20 tokens fits.  All calls on
+ * one device share that device's scratch: calls that may overlap on one
+ * device (other streams, other host threads) race and must be ordered by
+ * the caller. */
+hx_status hx_decode_attn_noalloc(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                                 const int64_t* ctx_len, float scale, float* o, float* lse, void* stream);
+
 /* A whole decode step in one call for callers that hold all slices on one
  * GPU: append each request's n_new newest rows, then hx_decode_attn.  The
  * new rows are rows [ctx_len[b] - n_new, ctx_len[b]) of request b, given in

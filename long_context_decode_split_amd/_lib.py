@@ -58,6 +58,7 @@ SIGNATURES = {
     "hx_workspace_init": (I32, [VP, SZ, VP]),
     "hx_decode_attn_partial": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_decode_attn": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_decode_attn_noalloc": (I32, [P_DESC, P_CACHE, VP, I32, P_I64, F32, VP, VP, VP]),
     "hx_lse_combine": (I32, [I32, I32, I32, I32, VP, VP, VP, VP, VP]),
     "hx_pool_layout": (I32, [P_DESC, I32, ctypes.POINTER(hx_kv_layout_info)]),
     "hx_kv_append_paged": (I32, [P_DESC, P_POOL, VP, VP, VP, VP, P_I64, P_I32, I32, VP]),

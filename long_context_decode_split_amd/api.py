@@ -18,7 +18,7 @@ from ._lib import (HX_FLAG_P_BF16, HX_KV_BF16, HX_KV_FP8_E4M3, HX_KV_MXFP4, HXEr
 __all__ = ["HXError", "HX_FLAG_P_BF16", "KVDesc", "KVCache", "KVPool", "DTYPES", "kv_layout", "pool_layout", "slot", "slice_len",
            "kv_tile_offset", "kv_append", "kv_append_bf16", "kv_dequant", "kv_append_paged", "kv_append_bf16_paged",
            "kv_dequant_paged", "workspace_size", "workspace_init", "decode_attn_partial", "decode_attn",
-           "decode_attn_partial_paged", "decode_attn_paged", "decode_step", "decode_step_paged", "lse_combine",
+           "decode_attn_noalloc", "decode_attn_partial_paged", "decode_attn_paged", "decode_step", "decode_step_paged", "lse_combine",
            "version", "exported_symbols"]
 
 DTYPES = {"bf16": HX_KV_BF16, "fp8_e4m3": HX_KV_FP8_E4M3, "mxfp4": HX_KV_MXFP4}
@@ -268,6 +268,14 @@ def decode_attn(cache: KVCache, q, ctx_len, scale, o, lse, ws, stream=None):
     check(lib().hx_decode_attn(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq, _i64(ctx_len),
                                float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)))
+
+
+def decode_attn_noalloc(cache: KVCache, q, ctx_len, scale, o, lse, stream=None):
+    """``hx_decode_attn_noalloc``: ``decode_attn`` on the library's fixed
+    per-device scratch (no workspace argument; calls on one device must not
+    overlap)."""
+    check(lib().hx_decode_attn_noalloc(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), q.shape[1],
+                                       _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def decode_attn_partial_paged(pool: KVPool, q, ctx_len, scale, o_part, lse_part, ws, stream=None):

@@ -194,9 +194,11 @@ struct WsLayout {
   int64_t total;
 };
 
-static WsLayout ws_layout(const hx_kv_desc& d, int kind, int G) {
+// `recs` split records: ws_records (the bound hx_workspace_size reports),
+// or the count one call actually uses (the fixed scratch of
+// hx_decode_attn_noalloc).
+static WsLayout ws_layout(const hx_kv_desc& d, int G, int64_t recs) {
   WsLayout w;
-  const int64_t recs = ws_records(d, kind);
   const int64_t Hq = (int64_t)G * d.Hkv;
   w.o_off = 0;
   w.lse_off = align256(recs * G * d.Dv * 4);
@@ -588,7 +590,7 @@ hx_status hx_workspace_size(const hx_kv_desc* desc, int32_t Hq, size_t* bytes) {
   if (s) return s;
   s = check_heads(*desc, geo, Hq);
   if (s) return s;
-  *bytes = (size_t)ws_layout(*desc, geo.kind, Hq / desc->Hkv).total;
+  *bytes = (size_t)ws_layout(*desc, Hq / desc->Hkv, ws_records(*desc, geo.kind)).total;
   return HX_OK;
 }
 
@@ -607,14 +609,70 @@ namespace hx {
 // slice's partial or split records straight into the final output.
 // With `fuse` (an append_setup result) and its host positions, the partial
 // kernels first append those rows into the tiles they own (hx_decode_step).
+// Split plan of the requests b0 .. b0 + nb - 1 of one launch: fills a.n,
+// a.cpw, a.waves, a.nsplit, a.wg_begin and a.fold_begin; returns the number
+// of workgroups (= split records) of the launch.  `final_out`: the one-call
+// forms, which fold every record in their second launch.
+static int plan_launch(const hx_kv_desc& d, const Geometry& geo, const int64_t* ctx_len, int b0, int nb, int G,
+                       bool final_out, PartialArgs& a) {
+  const int target = target_wgs(geo.kind, d.dtype);
+  // the one-call forms (fold launched anyway) take splits half as long:
+  // two tiles per wave (measured on the 4,096-token step: 30.2 -> 29.3 us)
+  const int minc = final_out ? std::max(1, min_chunks_per_wg(geo.kind) / 2) : min_chunks_per_wg(geo.kind);
+  int64_t W = 0;
+  int64_t nch[kMaxBatchPerLaunch];
+  for (int i = 0; i < nb; ++i) {
+    a.n[i] = ctx_len[b0 + i];
+    nch[i] = (slice_len(a.n[i], d.P, 0) + kChunk - 1) / kChunk;   // slice 0 is never shorter
+    W += nch[i] * d.Hkv * d.P;
+  }
+  int64_t nch_max = 1;
+  for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
+  int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
+  cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
+  // short contexts: slices of at most kShortSliceChunks tiles are not split
+  // (one workgroup per slice, no fold launch; measured faster on the
+  // 4,096-token single-request step, where fixed launch costs dominate).
+  // The one-call forms fold every record in their second launch anyway, so
+  // there short slices are split like long ones (HX_SHORT_ONE_CALL=1 keeps
+  // them whole: tuning knob).
+  const bool short_mode = nch_max <= kShortSliceChunks && (!final_out || env_int("HX_SHORT_ONE_CALL", 0, 0, 1));
+  if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
+  a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
+  if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
+  a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
+  int wgs = 0, folds = 0;
+  for (int i = 0; i < nb; ++i) {
+    a.nsplit[i] = (int)((nch[i] + a.cpw - 1) / a.cpw);
+    a.wg_begin[i] = wgs;
+    a.fold_begin[i] = folds;
+    wgs += a.nsplit[i] * d.Hkv * d.P;
+    if (a.nsplit[i] > 1) folds += d.Hkv * d.P * G;
+  }
+  a.wg_begin[nb] = wgs;
+  a.fold_begin[nb] = folds;
+  return wgs;
+}
+
+// Bytes of the library's fixed scratch, the workspace of
+// hx_decode_attn_noalloc (one array per device, held until the process
+// ends): enough for the split records and slice partials of every workload
+// here (the largest, 8 requests of 128 MLA heads at 2^20 tokens, uses about
+// 80 MiB).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+
 // With `check_only`, every argument is checked and nothing is launched.
+// With `tight`, the workspace holds just the split records this call uses
+// (the fixed scratch of hx_decode_attn_noalloc) instead of the bound that
+// hx_workspace_size reports.
 static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* q,
                              int32_t Hq, const int64_t* ctx_len, float scale, float* o_part, float* lse_part,
                              void* ws, size_t ws_bytes, void* stream, float* o_final, float* lse_final,
                              const AppendArgs* fuse = nullptr, const int64_t* fuse_pos = nullptr,
-                             bool check_only = false) {
+                             bool check_only = false, bool tight = false) {
   const bool final_out = o_final != nullptr;
-  if (!desc || !cache || !q || !ctx_len || !ws) return fail(HX_EINVAL, "null argument");
+  // (the fixed scratch's address is taken after the checks: none yet then)
+  if (!desc || !cache || !q || !ctx_len || (!ws && !(tight && check_only))) return fail(HX_EINVAL, "null argument");
   if (final_out ? !lse_final : (!o_part || !lse_part)) return fail(HX_EINVAL, "null argument");
   Geometry geo;
   hx_status s = geometry(*desc, &geo);
@@ -630,17 +688,30 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int G = Hq / d.Hkv;
-  const WsLayout wl = ws_layout(d, geo.kind, G);
-  if ((int64_t)ws_bytes < wl.total)
-    return fail(HX_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)wl.total);
-  if (final_out) {
-    o_part = (float*)((uint8_t*)ws + wl.opart_off);
-    lse_part = (float*)((uint8_t*)ws + wl.lpart_off);
-  }
   const int64_t nmax = (int64_t)d.P * d.cap;
   for (int b = 0; b < d.B; ++b)
     if (ctx_len[b] < 1 || ctx_len[b] > nmax)
       return fail(HX_EINVAL, "ctx_len[%d]=%lld must be in [1, P*cap=%lld]", b, (long long)ctx_len[b], (long long)nmax);
+  int64_t records = ws_records(d, geo.kind);
+  if (tight) {
+    records = 1;
+    for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
+      PartialArgs t{};
+      records = std::max<int64_t>(records, plan_launch(d, geo, ctx_len, b0, std::min(kMaxBatchPerLaunch, d.B - b0), G,
+                                                        final_out, t));
+    }
+  }
+  const WsLayout wl = ws_layout(d, G, records);
+  if ((int64_t)ws_bytes < wl.total) {
+    if (tight)
+      return fail(HX_EINVAL, "this call needs %lld bytes of scratch, more than the %zu bytes of the library's fixed "
+                  "scratch: call hx_decode_attn with a workspace instead", (long long)wl.total, ws_bytes);
+    return fail(HX_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)wl.total);
+  }
+  if (final_out) {
+    o_part = (float*)((uint8_t*)ws + wl.opart_off);
+    lse_part = (float*)((uint8_t*)ws + wl.lpart_off);
+  }
   if (check_only) return HX_OK;
 
   PartialArgs a{};
@@ -669,45 +740,9 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
   a.vs_tile = pr.stride[3];
   a.c2 = scale * 1.44269504088896341f;
   a.split_p = (d.flags & HX_FLAG_P_BF16) == 0;
-  const int64_t records = ws_records(d, geo.kind);
-  const int target = target_wgs(geo.kind, d.dtype);
-  // the one-call forms (fold launched anyway) take splits half as long:
-  // two tiles per wave (measured on the 4,096-token step: 30.2 -> 29.3 us)
-  const int minc = final_out ? std::max(1, min_chunks_per_wg(geo.kind) / 2) : min_chunks_per_wg(geo.kind);
   for (int b0 = 0; b0 < d.B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, d.B - b0);
-    int64_t W = 0;
-    int64_t nch[kMaxBatchPerLaunch];
-    for (int i = 0; i < nb; ++i) {
-      a.n[i] = ctx_len[b0 + i];
-      nch[i] = (slice_len(a.n[i], d.P, 0) + kChunk - 1) / kChunk;   // slice 0 is never shorter
-      W += nch[i] * d.Hkv * d.P;
-    }
-    int64_t nch_max = 1;
-    for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
-    int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
-    cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
-    // short contexts: slices of at most kShortSliceChunks tiles are not split
-    // (one workgroup per slice, no fold launch; measured faster on the
-    // 4,096-token single-request step, where fixed launch costs dominate).
-    // The one-call forms fold every record in their second launch anyway, so
-    // there short slices are split like long ones (HX_SHORT_ONE_CALL=1 keeps
-    // them whole: tuning knob).
-    const bool short_mode = nch_max <= kShortSliceChunks && (!final_out || env_int("HX_SHORT_ONE_CALL", 0, 0, 1));
-    if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
-    a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
-    if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
-    a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
-    int wgs = 0, folds = 0;
-    for (int i = 0; i < nb; ++i) {
-      a.nsplit[i] = (int)((nch[i] + a.cpw - 1) / a.cpw);
-      a.wg_begin[i] = wgs;
-      a.fold_begin[i] = folds;
-      wgs += a.nsplit[i] * d.Hkv * d.P;
-      if (a.nsplit[i] > 1) folds += d.Hkv * d.P * G;
-    }
-    a.wg_begin[nb] = wgs;
-    a.fold_begin[nb] = folds;
+    const int wgs = plan_launch(d, geo, ctx_len, b0, nb, G, final_out, a);
     if (wgs > records) return fail(HX_EINVAL, "internal: %d workgroups exceed the %lld workspace records", wgs, (long long)records);
     a.b0 = b0;
     a.nb = nb;
@@ -743,6 +778,56 @@ hx_status hx_decode_attn(const hx_kv_desc* desc, const hx_kv_cache* cache, const
   if (!o) return fail(HX_EINVAL, "null argument");
   return decode_step(desc, cache, PoolRef{nullptr, 0}, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream,
                      o, lse);
+}
+
+}  // extern "C"
+
+namespace hx {
+
+// The fixed scratch of hx_decode_attn_noalloc.  In host code `scratch` is a
+// host-side stand-in, not a device address: its device address (one per
+// GPU, each GPU holding its own copy) comes from hipGetSymbolAddress, taken
+// once per device on the entry point's first call there, and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static hx_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = -1;
+  hx_status s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (s) return s;
+  if (dev < 0 || dev >= 64) return fail(HX_EUNSUPPORTED, "device %d: at most 64 devices are supported", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    s = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (s) return s;
+    if (!p) return fail(HX_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return HX_OK;
+}
+
+}  // namespace hx
+
+extern "C" {
+
+hx_status hx_decode_attn_noalloc(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* q, int32_t Hq,
+                                 const int64_t* ctx_len, float scale, float* o, float* lse, void* stream) {
+  g_err[0] = 0;
+  if (!o) return fail(HX_EINVAL, "null argument");
+  // every argument (and the scratch size this call needs) first, then the
+  // device's scratch address, then the launches
+  hx_status s = decode_step(desc, cache, PoolRef{nullptr, 0}, q, Hq, ctx_len, scale, nullptr, nullptr, nullptr,
+                            kScratchBytes, stream, o, lse, nullptr, nullptr, true, true);
+  if (s) return s;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s) return s;
+  return decode_step(desc, cache, PoolRef{nullptr, 0}, q, Hq, ctx_len, scale, nullptr, nullptr, ws, kScratchBytes,
+                     stream, o, lse, nullptr, nullptr, false, true);
 }
 
 hx_status hx_decode_attn_partial_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* q, int32_t Hq,

@@ -253,6 +253,31 @@ def test_decode_step_argument_checks():
         assert call() == _lib.HX_EHIP
 
 
+def test_decode_attn_noalloc_argument_checks():
+    """The fixed-scratch entry point checks its arguments, and whether its
+    split records and slice partials fit the library's 128 MiB scratch,
+    before it touches the device."""
+    L = _lib.lib()
+
+    def call(d, cache, ctx, Hq, o=0x30000, lse=0x40000, q=0x10000):
+        c = (ctypes.c_int64 * len(ctx))(*ctx)
+        return L.hx_decode_attn_noalloc(ctypes.byref(d.c()), ctypes.byref(cache), _fake(q), Hq, c, ctypes.c_float(0.1),
+                                        _fake(o) if o else None, _fake(lse), None)
+
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
+    cache = _lib.hx_kv_cache(0x50000, 0x60000, None, None)
+    assert call(d, cache, (5, 17), 8, o=0) == _lib.HX_EINVAL
+    assert call(d, cache, (5, 17), 8, lse=0x40004) == _lib.HX_EINVAL      # misaligned
+    assert call(d, cache, (5, 0), 8) == _lib.HX_EINVAL                      # empty request
+    assert call(d, cache, (5, 17), 0) == _lib.HX_EINVAL                     # no query heads
+    # 64 requests x 128 MLA heads x 64 slices: slice partials alone are 1 GiB
+    big = api.KVDesc(P=64, B=64, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="bf16", cap=16)
+    rc = call(big, _lib.hx_kv_cache(0x50000, None, None, None), [100] * 64, 128)
+    assert rc == _lib.HX_EINVAL and b"fixed" in L.hx_last_error()
+    if not torch.cuda.is_available():
+        assert call(d, cache, (5, 17), 8) == _lib.HX_EHIP                   # valid arguments reach the device
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_partial_without_device_is_hx_ehip():
     d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)
