@@ -79,7 +79,9 @@ typedef enum {
 #define HX_FLAG_P_BF16 1
 
 /* Describes one KV cache (one layer).  Supported combinations:
- *   GQA: Dk = Dv = 128, v_alias_k = 0, dtype any, 1 <= G <= 16;
+ *   GQA: Dk = Dv = 128, v_alias_k = 0, dtype any, 1 <= G <= 128 (groups of
+ *        more than 16 query heads run a kernel that shares each tile pair
+ *        among the workgroup's waves through LDS);
  *   MLA: Dk = 576, Dv = 512, v_alias_k = 1 (V is the first 512 columns of
  *        the K row: one latent KV head), dtype HX_KV_BF16, G = 128.
  * Other combinations return HX_EUNSUPPORTED. */

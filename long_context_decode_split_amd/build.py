@@ -40,6 +40,7 @@ COMMON = [
 # MLA kernel needs the AGPRs for its 256-register accumulator.
 EXTRA = {
     "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_gqa_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

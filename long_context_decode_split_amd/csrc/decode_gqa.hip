@@ -31,16 +31,12 @@
 // appends a decode step's new rows into its tiles (hx_decode_step).
 
 #include "hx_append.h"
+#include "hx_gqa_frag.h"
 
 namespace hx {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-
+using namespace frag;
 
 // Chunk tiles a wave keeps in flight (register budget: 32 VGPRs per bf16 tile).
 #ifndef HX_GQA_TILES_BF16
@@ -75,75 +71,6 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-__device__ __forceinline__ s16x4 as_s16x4(uint32_t lo, uint32_t hi) {
-  uint2 t = make_uint2(lo, hi);
-  return __builtin_bit_cast(s16x4, t);
-}
-
-__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
-// Two fp32 -> packed bf16 pair, round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-
-// fp8 e4m3 byte pairs -> packed bf16 (exact: e4m3 values are bf16 values).
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
-
-// Two e2m1 codes of byte `sel` -> packed bf16, multiplied by `scale`.
-template <int SEL>
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
-}
-
-// e8m0 byte -> fp32 2^(E-127) by placing E in the fp32 exponent field: one
-// shift, no branch.  Exact for E = 1..254; E = 0 (2^-127, elements below
-// 3.6e-38 in magnitude) reads as 0 and E = 255 (NaN) as +inf, so such blocks
-// give zero resp. non-finite contributions.
-// Byte J of w is taken through a sub-dword operand select of the shift, so
-// the conversion is one instruction.
-template <int J>
-__device__ __forceinline__ float e8m0_byte(uint32_t w) {
-  uint32_t r;
-  if constexpr (J == 0)
-    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
-        : "=v"(r) : "v"(23u), "v"(w));
-  else if constexpr (J == 1)
-    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
-        : "=v"(r) : "v"(23u), "v"(w));
-  else if constexpr (J == 2)
-    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
-        : "=v"(r) : "v"(23u), "v"(w));
-  else
-    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
-        : "=v"(r) : "v"(23u), "v"(w));
-  return __uint_as_float(r);
-}
-
-// Byte j (a constant after unrolling) of w as 2^(byte - 127).
-__device__ __forceinline__ float e8m0_sel(uint32_t w, int j) {
-  switch (j) {
-    case 0: return e8m0_byte<0>(w);
-    case 1: return e8m0_byte<1>(w);
-    case 2: return e8m0_byte<2>(w);
-    default: return e8m0_byte<3>(w);
-  }
-}
-
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-// c + (sum of a packed bf16 pair), in fp32.
-__device__ __forceinline__ float add_bf16x2(uint32_t pair, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), kOnes2, c, false);
-}
 
 // Raw bytes of one chunk tile that a lane needs; FMT 0 bf16, 1 fp8, 2 MXFP4.
 template <int FMT>

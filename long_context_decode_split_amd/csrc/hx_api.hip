@@ -573,7 +573,8 @@ namespace hx {
 static hx_status check_heads(const hx_kv_desc& d, const Geometry& geo, int32_t Hq) {
   if (Hq < 1 || Hq % d.Hkv) return fail(HX_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", Hq, d.Hkv);
   const int G = Hq / d.Hkv;
-  if (geo.kind == 0 && G > 16) return fail(HX_EUNSUPPORTED, "GQA kernel takes at most 16 query heads per KV head (G=%d)", G);
+  if (geo.kind == 0 && G > kGqaWideMaxHeads)
+    return fail(HX_EUNSUPPORTED, "GQA kernels take at most %d query heads per KV head (G=%d)", kGqaWideMaxHeads, G);
   if (geo.kind == 1 && G != 128) return fail(HX_EUNSUPPORTED, "MLA kernel takes 128 query heads per latent head (G=%d)", G);
   return HX_OK;
 }
@@ -639,7 +640,7 @@ static int plan_launch(const hx_kv_desc& d, const Geometry& geo, const int64_t* 
   const bool short_mode = nch_max <= kShortSliceChunks && (!final_out || env_int("HX_SHORT_ONE_CALL", 0, 0, 1));
   if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
   a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
-  if (geo.kind == 1) cpw += cpw & 1;   // MLA tiles are pairs of chunk tiles
+  if (geo.kind == 1 || G > kGqaNarrowMaxHeads) cpw += cpw & 1;   // MLA and wide-GQA tiles come in pairs
   a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
   int wgs = 0, folds = 0;
   for (int i = 0; i < nb; ++i) {
@@ -748,8 +749,9 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     a.nb = nb;
     a.fused_append = fuse != nullptr;
     if (fuse) a.app = append_batch(*fuse, fuse_pos, nullptr, b0, nb);
-    hipError_t e = geo.kind == 0 ? launch_gqa_partial(a, d.dtype, (hipStream_t)stream)
-                                 : launch_mla_partial(a, (hipStream_t)stream);
+    hipError_t e = geo.kind == 1         ? launch_mla_partial(a, (hipStream_t)stream)
+                   : G > kGqaNarrowMaxHeads ? launch_gqa_wide(a, d.dtype, (hipStream_t)stream)
+                                            : launch_gqa_partial(a, d.dtype, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
     if (s) return s;
     s = final_out ? check_hip(launch_fold_combine(a, o_final, lse_final, (hipStream_t)stream), "fold/combine launch")

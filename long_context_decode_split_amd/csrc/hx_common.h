@@ -324,6 +324,11 @@ struct PartialArgs {
 HXHD TileMap tile_map(const PartialArgs& a) { return TileMap{a.table, a.num_blocks, a.P, a.Btot, a.Hkv, a.cap_chunks}; }
 
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
+// GQA groups of more than 16 query heads (decode_gqa_wide.hip): tiles in
+// pairs, so split sizes (cpw) are even.
+constexpr int kGqaNarrowMaxHeads = 16;
+constexpr int kGqaWideMaxHeads = 128;
+hipError_t launch_gqa_wide(const PartialArgs& a, int dtype, hipStream_t st);
 hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
 // Folds the split records of every slice with more than one split into the
 // slice outputs (o_part, lse_part); no-op when every slice has one split.

@@ -176,8 +176,10 @@ def test_desc_errors(bad, status):
 def test_workspace_size_and_heads():
     d = DESCS[0]
     assert api.workspace_size(d, 8) > 0
+    for G in (17, 34, 64, 128):        # wide GQA groups
+        assert api.workspace_size(api.KVDesc(**{**d.__dict__, "Hkv": 1}), G) > api.workspace_size(d, 8)
     with pytest.raises(api.HXError) as e:
-        api.workspace_size(d, 17 * 2)   # G = 34 > 16
+        api.workspace_size(api.KVDesc(**{**d.__dict__, "Hkv": 1}), 129)   # G = 129 > 128
     assert e.value.status == _lib.HX_EUNSUPPORTED
     with pytest.raises(api.HXError) as e:
         api.workspace_size(DESCS[1], 3)   # not a multiple of Hkv = 2
