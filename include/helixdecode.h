@@ -399,6 +399,34 @@ hx_status hx_block_pool_reserve(hx_block_pool* pool, const hx_kv_desc* desc, int
  * pool and the table unchanged. */
 hx_status hx_block_pool_release(hx_block_pool* pool, const hx_kv_desc* desc, int32_t* table_host, int32_t b);
 
+/* ------------------------------------------------------------------------
+ * Launch trace (for profiling; not needed to use the library)
+ *
+ * hx_trace_begin records a start event on `stream` and opens a trace; until
+ * hx_trace_end, every kernel the library launches (from any thread) is
+ * followed by a HIP event recorded on that launch's stream, for up to
+ * `capacity` (1 .. 2^20) launches.  hx_trace_end waits for the last event,
+ * closes the trace and reports, for launch i, its kernel's name (`names`:
+ * host char [capacity][32], NUL-terminated: "gqa_partial",
+ * "gqa_wide_partial", "mla_partial", "split_fold", "fold_combine",
+ * "lse_combine", "append", "quant_append", "dequant") and ms[i] (host float
+ * [capacity]): the time from the previous event (the start event for i = 0)
+ * to the end of launch i, which is the launch's duration when every traced
+ * launch is on `stream` and nothing else runs on it in between.  *n
+ * receives the number of launches.  HX_ENOSPC: more launches than
+ * `capacity` (the first `capacity` are reported); HX_EINVAL: a trace is
+ * already open (begin) or none is (end).  Events are host-side HIP objects
+ * created by hx_trace_begin and destroyed by hx_trace_end; do not open a
+ * trace around HIP graph capture.
+ * ------------------------------------------------------------------------ */
+hx_status hx_trace_begin(int32_t capacity, void* stream);
+/* Adds the caller's own entry `name` (at most 31 characters kept) to the
+ * open trace, recorded on `stream` now: it ends the interval of whatever
+ * the caller ran on the stream since the previous entry (HX_EINVAL when no
+ * trace is open). */
+hx_status hx_trace_mark(const char* name, void* stream);
+hx_status hx_trace_end(int32_t* n, float* ms, char* names);
+
 #ifdef __cplusplus
 }
 #endif

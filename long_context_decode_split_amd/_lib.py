@@ -73,6 +73,9 @@ SIGNATURES = {
     "hx_block_pool_free_count": (I32, [VP, P_I32]),
     "hx_block_pool_reserve": (I32, [VP, P_DESC, P_I32, I32, I64, P_I32]),
     "hx_block_pool_release": (I32, [VP, P_DESC, P_I32, I32]),
+    "hx_trace_begin": (I32, [I32, VP]),
+    "hx_trace_mark": (I32, [ctypes.c_char_p, VP]),
+    "hx_trace_end": (I32, [P_I32, ctypes.POINTER(F32), ctypes.c_char_p]),
 }
 
 _lib = None

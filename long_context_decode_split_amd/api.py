@@ -19,7 +19,7 @@ __all__ = ["HXError", "HX_FLAG_P_BF16", "KVDesc", "KVCache", "KVPool", "DTYPES",
            "kv_tile_offset", "kv_append", "kv_append_bf16", "kv_dequant", "kv_append_paged", "kv_append_bf16_paged",
            "kv_dequant_paged", "workspace_size", "workspace_init", "decode_attn_partial", "decode_attn",
            "decode_attn_noalloc", "decode_attn_partial_paged", "decode_attn_paged", "decode_step", "decode_step_paged", "lse_combine",
-           "version", "exported_symbols"]
+           "version", "exported_symbols", "Trace"]
 
 DTYPES = {"bf16": HX_KV_BF16, "fp8_e4m3": HX_KV_FP8_E4M3, "mxfp4": HX_KV_MXFP4}
 
@@ -316,3 +316,43 @@ def lse_combine(o_part, lse_part, o, lse, stream=None):
     o [B, Hq, Dv], lse [B, Hq] (all float32)."""
     P, B, Hq, Dv = o_part.shape
     check(lib().hx_lse_combine(P, B, Hq, Dv, _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+class Trace:
+    """``hx_trace_begin`` / ``hx_trace_end`` as a context manager: while it
+    is open, every library launch is followed by a HIP event on its stream.
+    ``launches`` then lists (kernel name, ms from the previous event to the
+    end of that launch)."""
+
+    NAME = 32
+
+    def __init__(self, capacity=4096, stream=None):
+        self.capacity = int(capacity)
+        self.stream = stream
+        self.launches = []
+
+    def __enter__(self):
+        check(lib().hx_trace_begin(self.capacity, _stream(self.stream)))
+        return self
+
+    def __exit__(self, *exc):
+        n = ctypes.c_int32()
+        ms = (ctypes.c_float * self.capacity)()
+        names = ctypes.create_string_buffer(self.capacity * self.NAME)
+        check(lib().hx_trace_end(ctypes.byref(n), ms, names))
+        raw = names.raw
+        self.launches = [(raw[i * self.NAME:(i + 1) * self.NAME].split(b"\0", 1)[0].decode(), float(ms[i]))
+                         for i in range(n.value)]
+        return False
+
+    def mark(self, name, stream=None):
+        """``hx_trace_mark``: an entry of the caller's own for the work it ran
+        on the stream since the previous entry."""
+        check(lib().hx_trace_mark(name.encode(), _stream(stream)))
+
+    def by_kernel(self):
+        """{kernel name: [ms of each launch]}"""
+        out = {}
+        for name, ms in self.launches:
+            out.setdefault(name, []).append(ms)
+        return out

@@ -49,4 +49,9 @@ FP8_GQA = Workload("fp8_gqa", B=32, Hq=16, Hkv=1, Dk=128, Dv=128, v_alias_k=Fals
 MXFP4_RAGGED = Workload("mxfp4_ragged", B=16, Hq=16, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="mxfp4", P=8,
                         ctx=None, ctx_range=(4096, 2 * 1024 * 1024))
 
-ALL = {w.name: w for w in (TINY_GQA, LLAMA405B_SHARE, DEEPSEEK_MLA, FP8_GQA, MXFP4_RAGGED)}
+# A wide GQA group (64 query heads on one KV head, e.g. Llama-405B's 128:8
+# at TPA = 2): both products dense enough for the matrix cores to matter.
+WIDE_GQA_G64 = Workload("wide_gqa_g64", B=8, Hq=64, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", P=8,
+                        ctx=1 << 20)
+
+ALL = {w.name: w for w in (TINY_GQA, LLAMA405B_SHARE, DEEPSEEK_MLA, FP8_GQA, MXFP4_RAGGED, WIDE_GQA_G64)}

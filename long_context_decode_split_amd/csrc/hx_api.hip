@@ -4,8 +4,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -32,6 +34,38 @@ hx_status check_hip(hipError_t e, const char* what) {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------- launch trace
+// While a trace is open (hx_trace_begin .. hx_trace_end), every kernel the
+// library launches is followed by a HIP event recorded on its stream, so the
+// events bracket the launches.
+struct Trace {
+  std::mutex mu;
+  bool open = false, overflow = false;
+  int cap = 0, n = 0;
+  hipEvent_t start = nullptr;
+  std::vector<hipEvent_t> ev;
+  std::vector<char> names;   // [cap][kTraceName]
+};
+constexpr int kTraceName = 32;
+static Trace g_trace;
+static std::atomic<bool> g_trace_open{false};
+
+static void trace_mark(const char* name, hipStream_t st) {
+  if (!g_trace_open.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (!g_trace.open) return;
+  if (g_trace.n >= g_trace.cap) {
+    g_trace.overflow = true;
+    return;
+  }
+  if (hipEventRecord(g_trace.ev[g_trace.n], st) != hipSuccess) {
+    g_trace.overflow = true;
+    return;
+  }
+  snprintf(&g_trace.names[(size_t)g_trace.n * kTraceName], kTraceName, "%s", name);
+  ++g_trace.n;
+}
 
 // Plane and tile sizes for `units` chunk tiles per plane (one plane for a
 // packed cache: its tiles hold all four parts).
@@ -393,6 +427,7 @@ static hx_status kv_append(const hx_kv_desc* desc, const hx_kv_cache* cache, Poo
     const AppendArgs a = append_batch(base, pos, count, b0, nb);
     s = check_hip(launch_append(a, nb, (hipStream_t)stream), "kv_append launch");
     if (s) return s;
+    if (a.max_chunks > 0) trace_mark("append", (hipStream_t)stream);
   }
   return HX_OK;
 }
@@ -457,6 +492,7 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
     a.src[1] = (const uint16_t*)v_new + off;
     s = check_hip(launch_quant_append(a, nb, (hipStream_t)stream), "kv_append_bf16 launch");
     if (s) return s;
+    trace_mark("quant_append", (hipStream_t)stream);
   }
   return HX_OK;
 }
@@ -497,7 +533,9 @@ static hx_status kv_dequant(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   a.g = g;
   a.j0 = j0;
   a.n = n;
-  return check_hip(launch_dequant(a, (hipStream_t)stream), "kv_dequant launch");
+  s = check_hip(launch_dequant(a, (hipStream_t)stream), "kv_dequant launch");
+  if (!s && n > 0) trace_mark("dequant", (hipStream_t)stream);
+  return s;
 }
 
 }  // namespace hx
@@ -754,9 +792,16 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
                                             : launch_gqa_partial(a, d.dtype, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
     if (s) return s;
+    if (wgs > 0)
+      trace_mark(geo.kind == 1 ? "mla_partial" : (G > kGqaNarrowMaxHeads ? "gqa_wide_partial" : "gqa_partial"),
+                 (hipStream_t)stream);
     s = final_out ? check_hip(launch_fold_combine(a, o_final, lse_final, (hipStream_t)stream), "fold/combine launch")
                   : check_hip(launch_split_fold(a, (hipStream_t)stream), "split fold launch");
     if (s) return s;
+    if (final_out)
+      trace_mark("fold_combine", (hipStream_t)stream);
+    else if (a.fold_begin[nb] > 0)
+      trace_mark("split_fold", (hipStream_t)stream);
   }
   return HX_OK;
 }
@@ -923,7 +968,74 @@ hx_status hx_lse_combine(int32_t P, int32_t B, int32_t Hq, int32_t Dv, const flo
   const void* ptrs[4] = {o_part, lse_part, o, lse};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
-  return check_hip(launch_lse_combine(P, B, Hq, Dv, o_part, lse_part, o, lse, (hipStream_t)stream), "lse_combine launch");
+  hx_status s = check_hip(launch_lse_combine(P, B, Hq, Dv, o_part, lse_part, o, lse, (hipStream_t)stream),
+                          "lse_combine launch");
+  if (!s) trace_mark("lse_combine", (hipStream_t)stream);
+  return s;
+}
+
+hx_status hx_trace_begin(int32_t capacity, void* stream) {
+  g_err[0] = 0;
+  if (capacity < 1 || capacity > (1 << 20)) return fail(HX_EINVAL, "capacity=%d must be in 1..2^20", capacity);
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.open) return fail(HX_EINVAL, "a trace is already open");
+  std::vector<hipEvent_t> ev;
+  hipEvent_t start = nullptr;
+  hx_status s = check_hip(hipEventCreate(&start), "hipEventCreate");
+  for (int i = 0; !s && i < capacity; ++i) {
+    hipEvent_t e = nullptr;
+    s = check_hip(hipEventCreate(&e), "hipEventCreate");
+    if (!s) ev.push_back(e);
+  }
+  if (!s) s = check_hip(hipEventRecord(start, (hipStream_t)stream), "hipEventRecord");
+  if (s) {
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+    if (start) hipEventDestroy(start);
+    return s;
+  }
+  g_trace.ev.swap(ev);
+  g_trace.start = start;
+  g_trace.names.assign((size_t)capacity * kTraceName, 0);
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.overflow = false;
+  g_trace.open = true;
+  g_trace_open.store(true, std::memory_order_release);
+  return HX_OK;
+}
+
+hx_status hx_trace_mark(const char* name, void* stream) {
+  g_err[0] = 0;
+  if (!name) return fail(HX_EINVAL, "null argument");
+  if (!g_trace_open.load(std::memory_order_acquire)) return fail(HX_EINVAL, "no trace is open");
+  trace_mark(name, (hipStream_t)stream);
+  return HX_OK;
+}
+
+hx_status hx_trace_end(int32_t* n, float* ms, char* names) {
+  g_err[0] = 0;
+  if (!n || !ms || !names) return fail(HX_EINVAL, "null argument");
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (!g_trace.open) return fail(HX_EINVAL, "no trace is open");
+  g_trace_open.store(false, std::memory_order_release);
+  g_trace.open = false;
+  hx_status s = HX_OK;
+  if (g_trace.n > 0) s = check_hip(hipEventSynchronize(g_trace.ev[g_trace.n - 1]), "hipEventSynchronize");
+  for (int i = 0; !s && i < g_trace.n; ++i)
+    s = check_hip(hipEventElapsedTime(&ms[i], i ? g_trace.ev[i - 1] : g_trace.start, g_trace.ev[i]),
+                  "hipEventElapsedTime");
+  if (!s) {
+    memcpy(names, g_trace.names.data(), (size_t)g_trace.n * kTraceName);
+    *n = g_trace.n;
+  }
+  for (hipEvent_t e : g_trace.ev) hipEventDestroy(e);
+  hipEventDestroy(g_trace.start);
+  g_trace.ev.clear();
+  g_trace.start = nullptr;
+  if (!s && g_trace.overflow)
+    return fail(HX_ENOSPC, "more launches than the trace's capacity of %d (the first %d are reported)", g_trace.cap,
+                g_trace.n);
+  return s;
 }
 
 }  // extern "C"

@@ -280,6 +280,19 @@ def test_decode_attn_noalloc_argument_checks():
         assert call(d, cache, (5, 17), 8) == _lib.HX_EHIP                   # valid arguments reach the device
 
 
+def test_trace_argument_checks():
+    L = _lib.lib()
+    n = ctypes.c_int32()
+    ms = (ctypes.c_float * 4)()
+    names = ctypes.create_string_buffer(4 * 32)
+    assert L.hx_trace_end(ctypes.byref(n), ms, names) == _lib.HX_EINVAL        # none open
+    assert L.hx_trace_mark(b"x", None) == _lib.HX_EINVAL                        # none open
+    assert L.hx_trace_begin(0, None) == _lib.HX_EINVAL
+    assert L.hx_trace_begin(1 << 21, None) == _lib.HX_EINVAL
+    if not torch.cuda.is_available():
+        assert L.hx_trace_begin(4, None) == _lib.HX_EHIP                       # events need a device
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_partial_without_device_is_hx_ehip():
     d = api.KVDesc(P=4, B=2, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)

@@ -121,3 +121,41 @@ def test_failed_mxfp4_step_leaves_the_cache_unchanged():
     torch.cuda.synchronize()
     for a, b in zip(snap, _planes(c)):
         assert torch.equal(a, b), "a refused step wrote the cache"
+
+
+def test_launch_trace_brackets_each_kernel():
+    """The library's launch trace: one entry per kernel launch, named, with
+    durations that add up to the step time measured around the calls."""
+    w = configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(20000, 60000))
+    inp = synth.make_inputs(w, 33, device=DEV)
+    desc = H.desc_of(inp)
+    c = api.KVCache(desc, device=DEV, fill=0xFF)
+    api.kv_append(c, inp.k, inp.v, None, None, pos=[0] * w.B, count=[n - 1 for n in inp.ctx])
+    new = [_newest(t, inp.ctx, 1) for t in (inp.k, inp.v)]
+    ws = torch.zeros(api.workspace_size(desc, w.Hq), dtype=torch.uint8, device=DEV)
+    o = torch.empty(w.B, w.Hq, w.Dv, device=DEV)
+    lse = torch.empty(w.B, w.Hq, device=DEV)
+    o_part = torch.empty(w.P, w.B, w.Hq, w.Dv, device=DEV)
+    lse_part = torch.empty(w.P, w.B, w.Hq, device=DEV)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with api.Trace(capacity=16) as tr:
+        a.record(st)
+        api.decode_step(c, *new, None, None, inp.q, inp.ctx, w.softmax_scale, o, lse, ws)
+        api.kv_append(c, *new, None, None, pos=[n - 1 for n in inp.ctx])
+        api.decode_attn_partial(c, inp.q, inp.ctx, w.softmax_scale, o_part, lse_part, ws)
+        api.lse_combine(o_part, lse_part, o, lse)
+        torch.ones(1000, device=DEV).sum()
+        tr.mark("user work")
+        b.record(st)
+        torch.cuda.synchronize()
+    names = [n for n, _ in tr.launches]
+    assert names == ["gqa_partial", "fold_combine", "append", "gqa_partial", "split_fold", "lse_combine", "user work"]
+    ms = [m for _, m in tr.launches]
+    assert all(m > 0 for m in ms[:6])
+    assert abs(sum(ms) - a.elapsed_time(b)) < 0.05 + 0.02 * a.elapsed_time(b)
+    with pytest.raises(api.HXError) as e:      # more launches than the capacity
+        with api.Trace(capacity=1):
+            api.decode_step(c, *new, None, None, inp.q, inp.ctx, w.softmax_scale, o, lse, ws)
+    assert e.value.status == 4
