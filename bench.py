@@ -392,6 +392,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(configs.ALL))
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="override the workload's query heads (GQA: a multiple of its KV heads, up to 128 per KV head)")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8_e4m3", "mxfp4"), default=None,
+                    help="override the workload's cache format (GQA workloads)")
     ap.add_argument("--no-extra", action="store_true",
                     help="measure only --workload (default: also every other workload, under \"workloads\")")
     ap.add_argument("--seed", type=int, default=0)
@@ -440,6 +444,12 @@ def main():
     t_start = time.time()
     flags = api.HX_FLAG_P_BF16 if args.p_bf16 else 0
     w = configs.ALL[args.workload]
+    if args.q_heads or args.kv_dtype:
+        if w.v_alias_k:
+            print("--q-heads / --kv-dtype apply to GQA workloads", file=sys.stderr)
+            sys.exit(2)
+        w = w.scaled(name=f"{w.name}+Hq{args.q_heads or w.Hq}+{args.kv_dtype or w.dtype}",
+                     Hq=args.q_heads or w.Hq, dtype=args.kv_dtype or w.dtype)
     head = measure(w, args, args.steps, args.warmup, args.append, args.attn, args.layout,
                    0 if args.no_cpu_baseline else args.cpu_budget, flags=flags, flush=args.flush_cache,
                    graph=args.graph)

@@ -72,10 +72,24 @@ template <>
 struct PairLay<2> {
   static constexpr int kBytes = 4352, kJobs = 4, kSc = 4096;
 };
-// Buffers in the ring (pairs in flight + the one in use): about 64 KiB or
-// less per workgroup, so two workgroups share a CU.
+// Buffers in the ring (pairs in flight + the one in use).  Each wave's work
+// on a pair is a chain of LDS reads, score products, softmax and value
+// products behind a barrier, so throughput comes from several workgroups per
+// CU rather than from a deep ring: measured at 2^20 tokens, 64 heads, bf16,
+// 4 workgroups per CU with two buffers (32 KiB) beat 2 with four (829 vs
+// 902 us on one box) and one workgroup with six (1,055 us); fp8 and MXFP4
+// pairs likewise run best with two buffers and eight workgroups per CU.
+#ifndef HX_WIDE_RING_BF16
+#define HX_WIDE_RING_BF16 2
+#endif
+#ifndef HX_WIDE_RING_FP8
+#define HX_WIDE_RING_FP8 2
+#endif
+#ifndef HX_WIDE_RING_FP4
+#define HX_WIDE_RING_FP4 2
+#endif
 template <int FMT>
-constexpr int kRing = FMT == 0 ? 4 : (FMT == 1 ? 6 : 8);
+constexpr int kRing = FMT == 0 ? HX_WIDE_RING_BF16 : (FMT == 1 ? HX_WIDE_RING_FP8 : HX_WIDE_RING_FP4);
 // Copy instructions each wave issues per pair: its code blocks plus (fp8,
 // MXFP4) its lanes of the scale copy.
 template <int FMT, int W>
@@ -529,8 +543,13 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
 template <int FMT, bool PAGED, bool FUSED>
 void launch_heads(const PartialArgs& a, int nwg, hipStream_t st) {
   const int nh = (a.G + 15) / 16;
+#ifndef HX_WIDE_TWO_WAVES
+#define HX_WIDE_TWO_WAVES 0
+#endif
   if (nh <= 2)
     hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 2, 1, FUSED>), dim3(nwg), dim3(128), 0, st, a);
+  else if (nh <= 4 && HX_WIDE_TWO_WAVES)
+    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 2, 2, FUSED>), dim3(nwg), dim3(128), 0, st, a);
   else if (nh <= 4)
     hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 4, 1, FUSED>), dim3(nwg), dim3(256), 0, st, a);
   else

@@ -190,7 +190,7 @@ static int device_cus() {
 
 constexpr int64_t kShortSliceChunks = 64;   // 1,024 rows per slice
 
-int target_wgs(int kind, int dtype) {
+int target_wgs(int kind, int dtype, int G) {
   // Workgroups per CU for one launch, measured on MI355X at 1M-token contexts:
   // bf16 / fp8 tiles stream best with two workgroups per CU (one round, all
   // resident); MXFP4 splits are short in time (a quarter of the bf16 bytes
@@ -198,7 +198,10 @@ int target_wgs(int kind, int dtype) {
   // rounds even (measured: 475 us at four, 445 us at eight on the ragged
   // 16-request cache).  The MLA kernel holds 152 KiB of LDS: one workgroup
   // of eight waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
-  const int dflt = kind != 0 ? 1 : (dtype == HX_KV_MXFP4 ? 8 : 2);
+  // Wide GQA groups (LDS-shared tile pairs, decode_gqa_wide.hip) run best
+  // with four workgroups per CU for bf16 and eight for fp8 and MXFP4 pairs.
+  const bool wide = kind == 0 && G > kGqaNarrowMaxHeads;
+  const int dflt = kind != 0 ? 1 : (dtype == HX_KV_MXFP4 ? 8 : (wide ? (dtype == HX_KV_BF16 ? 4 : 8) : 2));
   const int per_cu = env_int("HX_WGS_PER_CU", dflt, 1, 8);
   const int bound = kind == 0 ? kGqaTargetWgs : kMlaTargetWgs;
   return std::min(bound, device_cus() * per_cu);
@@ -654,7 +657,7 @@ namespace hx {
 // forms, which fold every record in their second launch.
 static int plan_launch(const hx_kv_desc& d, const Geometry& geo, const int64_t* ctx_len, int b0, int nb, int G,
                        bool final_out, PartialArgs& a) {
-  const int target = target_wgs(geo.kind, d.dtype);
+  const int target = target_wgs(geo.kind, d.dtype, G);
   // the one-call forms (fold launched anyway) take splits half as long:
   // two tiles per wave (measured on the 4,096-token step: 30.2 -> 29.3 us)
   const int minc = final_out ? std::max(1, min_chunks_per_wg(geo.kind) / 2) : min_chunks_per_wg(geo.kind);

@@ -353,7 +353,7 @@ constexpr int kGqaShortWaves = HX_GQA_SHORT_WAVES;
 constexpr int kGqaTargetWgs = 2048;   // upper bound on the split target
 constexpr int kMlaTargetWgs = 1024;
 constexpr int kMaxSplits = 256;       // splits per slice (the fold keeps their weights in LDS)
-int target_wgs(int kind, int dtype);  // device-dependent, <= the bounds above
+int target_wgs(int kind, int dtype, int G);  // device-dependent, <= the bounds above
 int min_chunks_per_wg(int kind);
 
 }  // namespace hx
