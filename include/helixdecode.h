@@ -292,6 +292,24 @@ hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const
                          const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* hx_decode_step with the step's new rows given as bf16 values (what the
+ * QKV projection produces: k_new [B][Hkv][n_new][Dk], v_new
+ * [B][Hkv][n_new][Dv], bf16, device; v_new NULL if v_alias_k), quantised
+ * into the cache's format inside the partial kernel by the workgroup that
+ * owns each new row's chunk tile, with the rules of hx_kv_append_bf16 (fp8:
+ * a group's scale grows and its stored codes are re-encoded when the new
+ * rows need it; MXFP4: per-row block exponents).  Two launches for any
+ * format: the partial kernel (which quantises first), then the fold into O
+ * and LSE.  The cache afterwards holds exactly what hx_kv_append_bf16
+ * writes, and O / LSE equal hx_kv_append_bf16 followed by hx_decode_attn.
+ * A bf16 cache takes the rows as storage format (= hx_decode_step).  Other
+ * arguments, checks and errors as hx_decode_step.  Helix summary,
+ * paragraphs on Helix's two layouts (new KV written round-robin as
+ * produced) and on KV parallelism. */
+hx_status hx_decode_step_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                              int32_t n_new, const void* q, int32_t Hq, const int64_t* ctx_len, float scale, float* o,
+                              float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* LSE-weighted combine of P partials (jaehun.me review, Prompt 1.3.2):
  *   m = max_r LSE_r, w_r = exp(LSE_r - m),
  *   o = sum_r w_r O_r / sum_r w_r,  lse = m + ln sum_r w_r.
@@ -364,7 +382,12 @@ hx_status hx_decode_attn_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, c
                                const int64_t* ctx_len, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
                                void* stream);
 
-/* hx_decode_step on a pool cache (the new rows' blocks must be listed). */
+/* hx_decode_step and hx_decode_step_bf16 on a pool cache (the new rows'
+ * blocks must be listed). */
+hx_status hx_decode_step_bf16_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new,
+                                    const void* v_new, int32_t n_new, const void* q, int32_t Hq,
+                                    const int64_t* ctx_len, float scale, float* o, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream);
 hx_status hx_decode_step_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new, const void* v_new,
                                const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q,
                                int32_t Hq, const int64_t* ctx_len, float scale, float* o, float* lse, void* ws,

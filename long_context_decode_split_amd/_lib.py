@@ -68,6 +68,8 @@ SIGNATURES = {
     "hx_decode_attn_paged": (I32, [P_DESC, P_POOL, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_decode_step": (I32, [P_DESC, P_CACHE, VP, VP, VP, VP, I32, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_decode_step_paged": (I32, [P_DESC, P_POOL, VP, VP, VP, VP, I32, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_decode_step_bf16": (I32, [P_DESC, P_CACHE, VP, VP, I32, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
+    "hx_decode_step_bf16_paged": (I32, [P_DESC, P_POOL, VP, VP, I32, VP, I32, P_I64, F32, VP, VP, VP, SZ, VP]),
     "hx_block_pool_create": (I32, [I32, ctypes.POINTER(VP)]),
     "hx_block_pool_destroy": (None, [VP]),
     "hx_block_pool_free_count": (I32, [VP, P_I32]),

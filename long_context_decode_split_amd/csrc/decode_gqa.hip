@@ -297,7 +297,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
 }
 
-template <int FMT, bool PAGED, int WAVES, bool FUSED>
+template <int FMT, bool PAGED, int WAVES, int FUSE>
 __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialArgs a) {
   constexpr int kWaves = WAVES;
   constexpr int kThreads = 64 * kWaves;
@@ -322,7 +322,9 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
   const int nch = (int)((L + kChunk - 1) / kChunk);
   const int c0 = split * a.cpw;
   const int c1 = min(c0 + a.cpw, nch);
-  if constexpr (FUSED) fused_append(a.app, bl, g, r, c0, c1);   // the step's new rows of these tiles first
+  // the step's new rows of these tiles first: copied (storage format) or quantised from bf16
+  if constexpr (FUSE == 1) fused_append(a.app, bl, g, r, c0, c1);
+  if constexpr (FUSE == 2) fused_quant(a.app, bl, g, r, c0, c1);
   const int tail_valid = (int)(L - (int64_t)(nch - 1) * kChunk);   // rows in the last chunk
 
   // Dense cache: the slice's tiles are consecutive from tile0.  Block pool:
@@ -498,28 +500,32 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
 
 }
 
-template <int FMT, bool PAGED, bool FUSED>
+template <int FMT, bool PAGED, int FUSE>
 void launch_waves(const PartialArgs& a, int nwg, hipStream_t st) {
   if (a.waves == kGqaShortWaves)
-    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaShortWaves, FUSED>), dim3(nwg), dim3(64 * kGqaShortWaves), 0,
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaShortWaves, FUSE>), dim3(nwg), dim3(64 * kGqaShortWaves), 0,
                        st, a);
   else
-    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaWavesPerWg, FUSED>), dim3(nwg), dim3(64 * kGqaWavesPerWg), 0,
+    hipLaunchKernelGGL((gqa_partial_kernel<FMT, PAGED, kGqaWavesPerWg, FUSE>), dim3(nwg), dim3(64 * kGqaWavesPerWg), 0,
                        st, a);
 }
 
-// MXFP4 has no fused variant: its loop lost 5% (dense) to 19% (block pool)
-// to the registers of the fused append, more than the append launch costs;
-// hx_decode_step appends MXFP4 rows with the append kernel instead.
+// Fused append modes per format: bf16 rows are the storage format (mode 1);
+// fp8 caches take stored codes (1) or bf16 rows to quantise (2); MXFP4
+// caches only the quantising mode (2): a step with stored MXFP4 codes runs
+// the append kernel first (the copy's registers slowed the kernel's loop by
+// 5% (dense) to 19% (block pool), more than the launch it saves).
 template <int FMT, bool PAGED>
 void launch_fmt(const PartialArgs& a, int nwg, hipStream_t st) {
-  if constexpr (FMT != 2) {
-    if (a.fused_append) {
-      launch_waves<FMT, PAGED, true>(a, nwg, st);
-      return;
-    }
+  if constexpr (FMT == 1) {
+    if (a.fused_append == 1) return launch_waves<FMT, PAGED, 1>(a, nwg, st);
   }
-  launch_waves<FMT, PAGED, false>(a, nwg, st);
+  if constexpr (FMT == 0) {
+    if (a.fused_append) return launch_waves<FMT, PAGED, 1>(a, nwg, st);
+  } else {
+    if (a.fused_append == 2) return launch_waves<FMT, PAGED, 2>(a, nwg, st);
+  }
+  launch_waves<FMT, PAGED, 0>(a, nwg, st);
 }
 
 }  // namespace

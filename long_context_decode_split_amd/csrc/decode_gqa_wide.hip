@@ -134,7 +134,7 @@ __device__ __forceinline__ void wait_pairs(int q) {
   }
 }
 
-template <int FMT, bool PAGED, int W, int NHW, bool FUSED>
+template <int FMT, bool PAGED, int W, int NHW, int FUSE>
 __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   using Lay = PairLay<FMT>;
@@ -163,7 +163,9 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
   const int nch = (int)((L + kChunk - 1) / kChunk);
   const int c0 = split * a.cpw;
   const int c1 = min(c0 + a.cpw, nch);
-  if constexpr (FUSED) fused_append(a.app, bl, g, r, c0, c1);   // the step's new rows of these tiles first
+  // the step's new rows of these tiles first: copied (storage format) or quantised from bf16
+  if constexpr (FUSE == 1) fused_append(a.app, bl, g, r, c0, c1);
+  if constexpr (FUSE == 2) fused_quant(a.app, bl, g, r, c0, c1);
   const int tail_valid = (int)(L - (int64_t)(nch - 1) * kChunk);   // rows in the slice's last chunk
   const int npairs = c1 > c0 ? (c1 - c0 + 1) >> 1 : 0;
   const int G = a.G;
@@ -540,33 +542,30 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
 #endif
 }
 
-template <int FMT, bool PAGED, bool FUSED>
+template <int FMT, bool PAGED, int FUSE>
 void launch_heads(const PartialArgs& a, int nwg, hipStream_t st) {
   const int nh = (a.G + 15) / 16;
-#ifndef HX_WIDE_TWO_WAVES
-#define HX_WIDE_TWO_WAVES 0
-#endif
   if (nh <= 2)
-    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 2, 1, FUSED>), dim3(nwg), dim3(128), 0, st, a);
-  else if (nh <= 4 && HX_WIDE_TWO_WAVES)
-    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 2, 2, FUSED>), dim3(nwg), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 2, 1, FUSE>), dim3(nwg), dim3(128), 0, st, a);
   else if (nh <= 4)
-    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 4, 1, FUSED>), dim3(nwg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 4, 1, FUSE>), dim3(nwg), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 4, 2, FUSED>), dim3(nwg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gqa_wide_kernel<FMT, PAGED, 4, 2, FUSE>), dim3(nwg), dim3(256), 0, st, a);
 }
 
-// MXFP4 has no fused variant (as in the narrow kernel): hx_decode_step
-// appends its rows with the append kernel first.
+// Fused append modes per format as in the narrow kernel: bf16 1; fp8 1 or 2;
+// MXFP4 only 2 (stored MXFP4 codes take the append kernel first).
 template <int FMT, bool PAGED>
 void launch_fmt_wide(const PartialArgs& a, int nwg, hipStream_t st) {
-  if constexpr (FMT != 2) {
-    if (a.fused_append) {
-      launch_heads<FMT, PAGED, true>(a, nwg, st);
-      return;
-    }
+  if constexpr (FMT == 1) {
+    if (a.fused_append == 1) return launch_heads<FMT, PAGED, 1>(a, nwg, st);
   }
-  launch_heads<FMT, PAGED, false>(a, nwg, st);
+  if constexpr (FMT == 0) {
+    if (a.fused_append) return launch_heads<FMT, PAGED, 1>(a, nwg, st);
+  } else {
+    if (a.fused_append == 2) return launch_heads<FMT, PAGED, 2>(a, nwg, st);
+  }
+  launch_heads<FMT, PAGED, 0>(a, nwg, st);
 }
 
 }  // namespace

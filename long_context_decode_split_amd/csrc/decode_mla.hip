@@ -440,7 +440,7 @@ hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
   const dim3 grid(nwg), block(kThreads);
-  const int v = (a.table ? 4 : 0) | (a.split_p ? 2 : 0) | (a.fused_append ? 1 : 0);
+  const int v = (a.table ? 4 : 0) | (a.split_p ? 2 : 0) | (a.fused_append == 1 ? 1 : 0);
   switch (v) {
     case 0: hipLaunchKernelGGL((mla_partial_kernel<false, false, false>), grid, block, 0, st, a); break;
     case 1: hipLaunchKernelGGL((mla_partial_kernel<false, false, true>), grid, block, 0, st, a); break;

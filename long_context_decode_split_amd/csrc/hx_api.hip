@@ -788,7 +788,7 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     if (wgs > records) return fail(HX_EINVAL, "internal: %d workgroups exceed the %lld workspace records", wgs, (long long)records);
     a.b0 = b0;
     a.nb = nb;
-    a.fused_append = fuse != nullptr;
+    a.fused_append = fuse ? (fuse->quant ? 2 : 1) : 0;
     if (fuse) a.app = append_batch(*fuse, fuse_pos, nullptr, b0, nb);
     hipError_t e = geo.kind == 1         ? launch_mla_partial(a, (hipStream_t)stream)
                    : G > kGqaNarrowMaxHeads ? launch_gqa_wide(a, d.dtype, (hipStream_t)stream)
@@ -938,9 +938,80 @@ static hx_status fused_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
                      pos.data());
 }
 
+// hx_decode_step_bf16: the step's new rows as bf16 values, quantised inside
+// the partial kernels by the workgroups that own their tiles (fp8, MXFP4);
+// a bf16 cache takes them as storage-format rows.
+static hx_status quant_step(const hx_kv_desc* desc, const hx_kv_cache* cache, PoolRef pool, const void* k_new,
+                            const void* v_new, int32_t n_new, const void* q, int32_t Hq, const int64_t* ctx_len,
+                            float scale, float* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!desc || !cache || !ctx_len || !o || !lse) return fail(HX_EINVAL, "null argument");
+  if (desc->dtype == HX_KV_BF16)
+    return fused_step(desc, cache, pool, k_new, v_new, nullptr, nullptr, n_new, q, Hq, ctx_len, scale, o, lse, ws,
+                      ws_bytes, stream);
+  Geometry g;
+  hx_status s = geometry(*desc, &g);
+  if (s) return s;
+  const hx_kv_desc& d = *desc;
+  if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
+  PlaneRefs pr;
+  s = plane_refs(d, g, cache, &pr);
+  if (s) return s;
+  // quantised caches are GQA caches (Dk = Dv = 128, separate V)
+  if (!k_new || !v_new) return fail(HX_EINVAL, "null k_new or v_new");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  std::vector<int64_t> pos((size_t)d.B);
+  for (int b = 0; b < d.B; ++b) {
+    if (ctx_len[b] < n_new)
+      return fail(HX_EINVAL, "ctx_len[%d]=%lld is shorter than the n_new=%d new rows", b, (long long)ctx_len[b], n_new);
+    pos[(size_t)b] = ctx_len[b] - n_new;
+  }
+  AppendArgs a{};
+  a.src[0] = (const uint8_t*)k_new;
+  a.src[1] = (const uint8_t*)v_new;
+  for (int i = 0; i < 4; ++i) {
+    a.dst[i] = pr.base[i];
+    a.tile_stride[i] = pr.stride[i];
+  }
+  a.lay[0] = g.lay_k;
+  a.lay[1] = g.lay_v;
+  a.width[0] = a.width[1] = d.Dk;
+  a.src_row_bytes[0] = a.src_row_bytes[1] = (int64_t)d.Dk * 2;   // bf16 rows
+  a.nplanes = 2;
+  a.P = d.P;
+  a.B = d.B;
+  a.Hkv = d.Hkv;
+  a.cap_chunks = d.cap / kChunk;
+  a.table = pool.table;
+  a.num_blocks = pool.num_blocks;
+  a.n_new = n_new;
+  a.quant = d.dtype;
+  return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse, &a,
+                     pos.data());
+}
+
 }  // namespace hx
 
 extern "C" {
+
+hx_status hx_decode_step_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
+                              int32_t n_new, const void* q, int32_t Hq, const int64_t* ctx_len, float scale, float* o,
+                              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return quant_step(desc, cache, PoolRef{nullptr, 0}, k_new, v_new, n_new, q, Hq, ctx_len, scale, o, lse, ws, ws_bytes,
+                    stream);
+}
+
+hx_status hx_decode_step_bf16_paged(const hx_kv_desc* desc, const hx_kv_pool* pool, const void* k_new,
+                                    const void* v_new, int32_t n_new, const void* q, int32_t Hq,
+                                    const int64_t* ctx_len, float scale, float* o, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  PoolRef ref;
+  hx_status s = check_pool(desc, pool, &ref);
+  if (s) return s;
+  return quant_step(desc, &pool->planes, ref, k_new, v_new, n_new, q, Hq, ctx_len, scale, o, lse, ws, ws_bytes,
+                    stream);
+}
 
 hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
                          const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q, int32_t Hq,

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "hx_common.h"
+#include "hx_quant.h"
 
 namespace hx {
 
@@ -245,6 +246,43 @@ __device__ __forceinline__ void fused_append(const AppendArgs& a, int bl, int g,
   for (int64_t c = first; c <= cl; c += a.P) {
     if (c / a.P < c0 || c / a.P >= c1) continue;
     append_rows(a, bl, g, c, threadIdx.x, blockDim.x);
+  }
+  __syncthreads();
+}
+
+// Fused quantising decode step: as fused_append, with the step's new rows
+// given as bf16 values (a.quant set) and quantised by the owning workgroup
+// into its tiles (quant_tile: the fp8 group's scale grows and its stored
+// codes are re-encoded when the new rows need it), K tile then V tile of
+// each touched group; then a workgroup barrier before any tile is read.
+// Uniform over the workgroup.
+__device__ __forceinline__ void fused_quant(const AppendArgs& a, int bl, int g, int r, int64_t c0, int64_t c1) {
+  const int64_t pos = a.pos[bl], end = pos + a.count[bl];
+  if (end <= pos || c1 <= c0) return;
+  const int64_t cf = pos / kChunk, cl = (end - 1) / kChunk;
+  const int64_t first = cf + ((r - cf % a.P) % a.P + a.P) % a.P;   // first group of slice r at or after cf
+  bool mine = false;
+  for (int64_t c = first; c <= cl; c += a.P) mine |= c / a.P >= c0 && c / a.P < c1;
+  if (!mine) return;
+  __shared__ float s_red[16];
+  __shared__ uint8_t s_e[kChunk][4];
+  const int D = a.width[0];
+  for (int64_t c = first; c <= cl; c += a.P) {
+    if (c / a.P < c0 || c / a.P >= c1) continue;
+    const int64_t row0 = c * kChunk;
+    const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, a.b0 + bl, g, c / a.P);
+    for (int p = 0; p < 2; ++p) {
+      QuantJob j;
+      j.src = reinterpret_cast<const uint16_t*>(a.src[p]) + (((int64_t)bl * a.Hkv + g) * a.n_new + (row0 - pos)) * D;
+      j.tile = a.dst[p] + tile * a.tile_stride[p];
+      j.sc = a.dst[2 + p] + tile * a.tile_stride[2 + p];
+      j.lay = a.lay[p];
+      j.D = D;
+      j.dtype = a.quant;
+      j.m_lo = (int)(pos > row0 ? pos - row0 : 0);
+      j.m_hi = (int)(end - row0 < kChunk ? end - row0 : kChunk);
+      quant_tile(j, threadIdx.x, blockDim.x, s_red, s_e);
+    }
   }
   __syncthreads();
 }

@@ -293,6 +293,11 @@ struct AppendArgs {
   int64_t pos[kMaxBatchPerLaunch];
   int32_t count[kMaxBatchPerLaunch];
   int b0;                  // first request of this launch
+  // 0: src holds storage-format rows, copied.  HX_KV_FP8_E4M3 / HX_KV_MXFP4:
+  // src[0], src[1] hold bf16 K and V rows (width[0] = D), quantised into the
+  // code planes dst[0], dst[1] and the scale planes dst[2], dst[3]
+  // (quant_tile in hx_quant.h)
+  int quant;
 };
 
 struct PartialArgs {
@@ -312,7 +317,8 @@ struct PartialArgs {
   int64_t k_tile, v_tile, ks_tile, vs_tile;   // bytes between consecutive tiles of each plane
   float c2;                // softmax scale * log2(e)
   int split_p;             // MLA: P as bf16 high part + residual (else rounded once)
-  int fused_append;        // the workgroups first append app's rows into the tiles they own
+  int fused_append;        // the workgroups first append app's rows into the tiles they own:
+                           // 0 no, 1 storage-format rows, 2 bf16 rows quantised (app.quant)
   AppendArgs app;          // (same requests as this launch: app.b0 = b0)
   int cpw;                 // chunks per workgroup (split size)
   int waves;               // GQA: waves per workgroup (kGqaWavesPerWg, or kGqaShortWaves for unsplit slices)
