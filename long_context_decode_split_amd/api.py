@@ -113,9 +113,13 @@ class KVCache:
         self.v = plane(lay["v_bytes"])
         self.k_scale = plane(lay["k_scale_bytes"])
         self.v_scale = plane(lay["v_scale_bytes"])
+        # the C structs of this cache, built once (the planes never move)
+        self._desc_ref = ctypes.byref(desc.c())
+        self._c = hx_kv_cache(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale))
+        self._ref = ctypes.byref(self._c)
 
     def c(self):
-        return hx_kv_cache(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale))
+        return self._c
 
     def nbytes(self):
         return sum(t.numel() for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None)
@@ -204,7 +208,7 @@ def kv_append(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, pos, count
     [B, Hkv, n_new, ...]; ``pos`` (and ``count``) are host sequences of B ints."""
     n_new = k_new.shape[2]
     cnt = None if count is None else (ctypes.c_int32 * len(count))(*[int(c) for c in count])
-    check(lib().hx_kv_append(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+    check(lib().hx_kv_append(cache._desc_ref, cache._ref, _ptr(k_new), _ptr(v_new),
                              _ptr(k_scale_new), _ptr(v_scale_new), _i64(pos), cnt, n_new, _stream(stream)))
 
 
@@ -255,7 +259,7 @@ def decode_attn_partial(cache: KVCache, q, ctx_len, scale, o_part, lse_part, ws,
     """``hx_decode_attn_partial``: q bf16 [B, Hq, Dk] -> o_part f32
     [P, B, Hq, Dv], lse_part f32 [P, B, Hq]."""
     Hq = q.shape[1]
-    check(lib().hx_decode_attn_partial(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq,
+    check(lib().hx_decode_attn_partial(cache._desc_ref, cache._ref, _ptr(q), Hq,
                                        _i64(ctx_len), float(scale), _ptr(o_part), _ptr(lse_part), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -265,7 +269,7 @@ def decode_attn(cache: KVCache, q, ctx_len, scale, o, lse, ws, stream=None):
     [B, Hq] (the whole step).  ``ws`` is scratch of ``workspace_size`` bytes;
     it needs no initialisation."""
     Hq = q.shape[1]
-    check(lib().hx_decode_attn(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(q), Hq, _i64(ctx_len),
+    check(lib().hx_decode_attn(cache._desc_ref, cache._ref, _ptr(q), Hq, _i64(ctx_len),
                                float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)))
 
@@ -296,7 +300,7 @@ def decode_step(cache: KVCache, k_new, v_new, k_scale_new, v_scale_new, q, ctx_l
     """``hx_decode_step``: append the newest ``k_new.shape[2]`` rows of every
     request (storage format, [B, Hkv, n_new, ...]) and attend: o f32
     [B, Hq, Dv], lse f32 [B, Hq]."""
-    check(lib().hx_decode_step(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+    check(lib().hx_decode_step(cache._desc_ref, cache._ref, _ptr(k_new), _ptr(v_new),
                                _ptr(k_scale_new), _ptr(v_scale_new), k_new.shape[2], _ptr(q), q.shape[1],
                                _i64(ctx_len), float(scale), _ptr(o), _ptr(lse), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
@@ -315,7 +319,7 @@ def decode_step_bf16(cache: KVCache, k_new, v_new, q, ctx_len, scale, o, lse, ws
     """``hx_decode_step_bf16``: the newest ``k_new.shape[2]`` rows of every
     request as bf16 [B, Hkv, n_new, D], quantised into the cache's format
     inside the step, then attention: o f32 [B, Hq, Dv], lse f32 [B, Hq]."""
-    check(lib().hx_decode_step_bf16(ctypes.byref(cache.desc.c()), ctypes.byref(cache.c()), _ptr(k_new), _ptr(v_new),
+    check(lib().hx_decode_step_bf16(cache._desc_ref, cache._ref, _ptr(k_new), _ptr(v_new),
                                     k_new.shape[2], _ptr(q), q.shape[1], _i64(ctx_len), float(scale), _ptr(o),
                                     _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
