@@ -35,6 +35,8 @@
 #include "hx_append.h"
 #include "hx_gqa_frag.h"
 
+#include <type_traits>
+
 namespace hx {
 namespace {
 
@@ -279,7 +281,10 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
   const float c2 = a.c2;
 
   // ---- one pair from LDS: scores, softmax, value product
-  auto compute = [&](const lds_u8* pb, int v0, int v1) {
+  // FULL: both tiles hold 16 valid rows, so no row is masked (MXFP4 only,
+  // where the masking is a measurable share of the issue slots)
+  auto compute = [&](auto full_t, const lds_u8* pb, int v0, int v1) {
+    constexpr bool FULL = decltype(full_t)::value;
     // K fragments of both tiles as bf16, and the per-tile scales
     bf16x8 kf[2][4];
     float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
@@ -349,8 +354,8 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
       const int vv[2] = {v0, v1};
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        keep01[t] = (4 * h + 0 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 1 < vv[t] ? 0xffff0000u : 0u);
-        keep23[t] = (4 * h + 2 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 3 < vv[t] ? 0xffff0000u : 0u);
+        keep01[t] = FULL ? ~0u : (4 * h + 0 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 1 < vv[t] ? 0xffff0000u : 0u);
+        keep23[t] = FULL ? ~0u : (4 * h + 2 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 3 < vv[t] ? 0xffff0000u : 0u);
       }
     }
 
@@ -367,10 +372,12 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) s8[4 * t + j] = FMT == 1 ? sc[j] * (c2 * ks[t]) : sc[j];
       }
+      if constexpr (!FULL) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (4 * h + j >= v0) s8[j] = -INFINITY;
-        if (4 * h + j >= v1) s8[4 + j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+          if (4 * h + j >= v0) s8[j] = -INFINITY;
+          if (4 * h + j >= v1) s8[4 + j] = -INFINITY;
+        }
       }
       // ---- online softmax (base 2): the reference moves only when some
       //      head's scores exceed it by more than the headroom
@@ -466,7 +473,7 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float v = p[4 * t + j] * e8m0_sel(vw[t][j], blk);
-              ps[4 * t + j] = 4 * h + j < (t ? v1 : v0) ? v : 0.f;   // rows past the slice: any scale byte
+              ps[4 * t + j] = FULL || 4 * h + j < (t ? v1 : v0) ? v : 0.f;   // rows past the slice: any scale byte
             }
           const bf16x8 PB = as_bf16x8(make_uint4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]),
                                                  pack_bf16(ps[4], ps[5]), pack_bf16(ps[6], ps[7])));
@@ -511,7 +518,15 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
     const int ct = c0 + 2 * k;
     const int v0 = ct == nch - 1 ? tail_valid : kChunk;
     const int v1 = ct + 1 < c1 ? (ct + 1 == nch - 1 ? tail_valid : kChunk) : 0;
-    compute((const lds_u8*)&s_buf[k % kNBuf][0], v0, v1);
+    const lds_u8* pb = (const lds_u8*)&s_buf[k % kNBuf][0];
+    if constexpr (FMT == 2) {
+      if (v0 == kChunk && v1 == kChunk)
+        compute(std::true_type{}, pb, v0, v1);
+      else
+        compute(std::false_type{}, pb, v0, v1);
+    } else {
+      compute(std::false_type{}, pb, v0, v1);
+    }
   }
 
   // ---- finalize this wave's heads (no exchange between waves)
