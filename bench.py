@@ -239,30 +239,63 @@ def cpu_baseline(inp, budget_s, o, lse):
 
 
 def time_steps(step, steps, warmup, stream, flush=None):
-    """Warm-up, then `steps` timed steps inside a launch trace.  Returns
-    (ms per step, per-step ms list, {kernel: [ms per launch]})."""
+    """Warm-up, then three passes of `steps` steps each.  Returns (ms per
+    step, per-step ms list, {kernel: [ms per launch]}):
+      * the timed region: `steps` back-to-back steps between two events and
+        nothing else on the stream (with `flush`: each step between its own
+        events, a cache flush before it, and the mean of those);
+      * per-step events around each step (the distribution);
+      * the library's launch trace, with the queue first filled by a plain
+        read of 2 GiB so the host runs ahead of the GPU: each launch's entry
+        is then its kernel's duration plus the dispatch gap before it, not
+        time the GPU spent waiting for the host."""
     for _ in range(warmup):
         step(stream)
     torch.cuda.synchronize()
     new_ev = lambda: torch.cuda.Event(enable_timing=True)
-    sev = [(new_ev(), new_ev()) for _ in range(steps)]
     start, end = new_ev(), new_ev()
-    torch.cuda.synchronize()
-    with api.Trace(capacity=8 * steps + 8, stream=stream) as tr:
-        start.record(stream)
+    sev = [(new_ev(), new_ev()) for _ in range(steps)]
+
+    def per_step(flush_marks=None):
         for i in range(steps):
             if flush is not None:
                 flush.fill_(i & 0xFF)
-                tr.mark("flush", stream)      # so the step's first launch is timed from here
+                if flush_marks is not None:
+                    flush_marks.mark("flush", stream)   # the step's first launch is timed from here
             sev[i][0].record(stream)
             step(stream)
             sev[i][1].record(stream)
+
+    torch.cuda.synchronize()
+    if flush is None:
+        start.record(stream)
+        for _ in range(steps):
+            step(stream)
         end.record(stream)
         torch.cuda.synchronize()
-    each = [a.elapsed_time(b) for a, b in sev]
-    total = float(np.mean(each)) if flush is not None else start.elapsed_time(end) / steps
+        total = start.elapsed_time(end) / steps
+        per_step()
+        torch.cuda.synchronize()
+        each = [a.elapsed_time(b) for a, b in sev]
+    else:
+        per_step()
+        torch.cuda.synchronize()
+        each = [a.elapsed_time(b) for a, b in sev]
+        total = float(np.mean(each))
+    primer = torch.empty(2 << 30, dtype=torch.uint8, device="cuda") if flush is None else None
+    torch.cuda.synchronize()
+    with api.Trace(capacity=8 * steps + 8, stream=stream) as tr:
+        if primer is not None:
+            api.read_probe(primer, stream=stream)
+            for _ in range(steps):
+                step(stream)
+        else:
+            per_step(tr)
+        torch.cuda.synchronize()
+    del primer
     kern = tr.by_kernel()
     kern.pop("flush", None)
+    kern.pop("read_probe", None)
     return total, each, kern
 
 
@@ -340,7 +373,10 @@ def measure(w, args, steps, warmup, append, attn, layout, cpu_budget, flags=0, f
             "algorithmic_flops": flops,
         },
         "timing_us": {"step": pct(each), "partial": pct(part),
-                      "cache": "flushed before every step" if flush else "hot (back-to-back steps)"},
+                      "cache": "flushed before every step" if flush else "hot (back-to-back steps)",
+                      "how": "step_us: the timed region (back-to-back steps between two events); step: each step "
+                             "between its own events; partial and kernels_us: the launch trace with the queue "
+                             "filled ahead (kernel duration plus the dispatch gap before it)"},
     }
     if graph_ms is not None:
         res["graph_step_us"] = round(graph_ms * 1e3, 2)
@@ -359,7 +395,7 @@ def measure(w, args, steps, warmup, append, attn, layout, cpu_budget, flags=0, f
 
 def copy_rates(nbytes=4 << 30, reps=5):
     """Same-run device-to-device copy (bytes read + written per second) and a
-    plain read-only reduction rate, as context for the HBM ceiling."""
+    plain streaming read (hx_read_probe), as context for the HBM ceiling."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -371,19 +407,19 @@ def copy_rates(nbytes=4 << 30, reps=5):
     b.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    x = src.view(torch.int32)
-    x.sum()
+    out = api.read_probe(src)
     torch.cuda.synchronize()
     a.record()
     for _ in range(reps):
-        x.sum()
+        api.read_probe(src, out)
     b.record()
     torch.cuda.synchronize()
     read_gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst, x
+    del src, dst, out
     torch.cuda.empty_cache()
     return {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1), "bytes": nbytes,
-            "how": "torch copy_ of 4 GiB (read + write bytes) and torch sum of the same 4 GiB (read), HIP events"}
+            "how": "torch copy_ of 4 GiB (read + write bytes) and hx_read_probe, a plain streaming read of the "
+                   "same 4 GiB with the kernels' 16-byte non-temporal loads (read bytes), HIP events"}
 
 
 def main():
@@ -461,7 +497,7 @@ def main():
             extras[name] = measure(configs.ALL[name], args, args.steps, args.warmup, args.append, args.attn,
                                    args.layout, 0 if args.no_cpu_baseline else args.extra_cpu_budget, flags=flags)
     rates = copy_rates()
-    log(f"[bench] device copy {rates['copy_gbs']:.0f} GB/s (read + write), read-only reduction "
+    log(f"[bench] device copy {rates['copy_gbs']:.0f} GB/s (read + write), plain streaming read "
         f"{rates['read_gbs']:.0f} GB/s; run took {time.time() - t_start:.0f}s")
 
     step_us = head["step_us"]

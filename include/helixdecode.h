@@ -450,6 +450,22 @@ hx_status hx_trace_begin(int32_t capacity, void* stream);
 hx_status hx_trace_mark(const char* name, void* stream);
 hx_status hx_trace_end(int32_t* n, float* ms, char* names);
 
+/* ------------------------------------------------------------------------
+ * Read probe (a measurement aid; not needed to use the library)
+ *
+ * Every kernel of the decode path is bound by reading the KV cache from HBM
+ * once, so its rate is best judged against what a plain read reaches on the
+ * same device.  hx_read_probe reads `nbytes` (a positive multiple of 16) of
+ * device memory at `src` (16-byte aligned) once, in 16-byte non-temporal
+ * loads per lane (1 KiB per wave-wide load, as the attention kernels load
+ * their tiles), and writes to out[i] (device uint32 [HX_READ_PROBE_BLOCKS])
+ * the XOR of the 32-bit words workgroup i read.  Asynchronous on `stream`;
+ * a traced launch is named "read_probe".  HX_EINVAL: null or misaligned
+ * pointer, or nbytes not a positive multiple of 16.
+ * ------------------------------------------------------------------------ */
+#define HX_READ_PROBE_BLOCKS 1024
+hx_status hx_read_probe(const void* src, int64_t nbytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,7 +78,10 @@ SIGNATURES = {
     "hx_trace_begin": (I32, [I32, VP]),
     "hx_trace_mark": (I32, [ctypes.c_char_p, VP]),
     "hx_trace_end": (I32, [P_I32, ctypes.POINTER(F32), ctypes.c_char_p]),
+    "hx_read_probe": (I32, [VP, I64, VP, VP]),
 }
+
+HX_READ_PROBE_BLOCKS = 1024
 
 _lib = None
 

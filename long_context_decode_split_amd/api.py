@@ -377,3 +377,15 @@ class Trace:
         for name, ms in self.launches:
             out.setdefault(name, []).append(ms)
         return out
+
+
+def read_probe(src, out=None, stream=None):
+    """``hx_read_probe``: one plain streaming read of the device tensor
+    ``src`` (its bytes, a multiple of 16); returns ``out``, a uint32 tensor
+    of ``HX_READ_PROBE_BLOCKS`` per-workgroup XORs of what was read."""
+    from ._lib import HX_READ_PROBE_BLOCKS
+    nbytes = src.numel() * src.element_size()
+    if out is None:
+        out = torch.empty(HX_READ_PROBE_BLOCKS, dtype=torch.int32, device=src.device)
+    check(lib().hx_read_probe(src.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+    return out

@@ -1112,4 +1112,16 @@ hx_status hx_trace_end(int32_t* n, float* ms, char* names) {
   return s;
 }
 
+hx_status hx_read_probe(const void* src, int64_t nbytes, uint32_t* out, void* stream) {
+  g_err[0] = 0;
+  if (!src || !out) return fail(HX_EINVAL, "null argument");
+  if (!aligned16(src)) return fail(HX_EINVAL, "src must be 16-byte aligned");
+  if (nbytes <= 0 || nbytes % 16 != 0) return fail(HX_EINVAL, "nbytes=%lld must be a positive multiple of 16",
+                                                   (long long)nbytes);
+  hx_status s = check_hip(launch_read_probe(src, nbytes, out, HX_READ_PROBE_BLOCKS, (hipStream_t)stream),
+                          "read_probe launch");
+  if (!s) trace_mark("read_probe", (hipStream_t)stream);
+  return s;
+}
+
 }  // extern "C"

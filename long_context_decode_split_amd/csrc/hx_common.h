@@ -348,6 +348,10 @@ hipError_t launch_fold_combine(const PartialArgs& a, float* o, float* lse, hipSt
 hipError_t launch_lse_combine(int P, int B, int Hq, int Dv, const float* o_part, const float* lse_part, float* o,
                               float* lse, hipStream_t st);
 
+// Plain streaming read of nbytes (a multiple of 16) by nblocks workgroups;
+// out[i] receives the XOR of what workgroup i read (read_probe.hip).
+hipError_t launch_read_probe(const void* src, int64_t nbytes, uint32_t* out, int nblocks, hipStream_t st);
+
 // Split policy shared by hx_workspace_size and hx_decode_attn_partial.
 constexpr int kGqaWavesPerWg = 4;
 // Short slices (not split) are latency-bound: their one workgroup per slice

@@ -35,6 +35,16 @@ def test_header_and_binding_agree():
     assert declared_symbols() == sorted(_lib.SIGNATURES), (declared_symbols(), sorted(_lib.SIGNATURES))
 
 
+def test_header_and_binding_constants_agree():
+    """Every #define HX_... and enumerator of the header has the binding's value."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(HX_[A-Z0-9_]+)\s+(\d+)\s*$", text, re.M)}
+    consts.update({m.group(1): int(m.group(2)) for m in re.finditer(r"\b(HX_[A-Z0-9_]+)\s*=\s*(\d+)", text)})
+    for name in ("HX_OK", "HX_EINVAL", "HX_EUNSUPPORTED", "HX_EHIP", "HX_ENOSPC", "HX_KV_BF16", "HX_KV_FP8_E4M3",
+                 "HX_KV_MXFP4", "HX_FLAG_P_BF16", "HX_READ_PROBE_BLOCKS"):
+        assert consts[name] == getattr(_lib, name), name
+
+
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\b(hx_[a-z_0-9]+)$", out, flags=re.M))
@@ -291,6 +301,18 @@ def test_trace_argument_checks():
     assert L.hx_trace_begin(1 << 21, None) == _lib.HX_EINVAL
     if not torch.cuda.is_available():
         assert L.hx_trace_begin(4, None) == _lib.HX_EHIP                       # events need a device
+
+
+def test_read_probe_argument_checks():
+    L = _lib.lib()
+    out = 0x80000
+    assert L.hx_read_probe(None, 1024, out, None) == _lib.HX_EINVAL
+    assert L.hx_read_probe(0x40000, 1024, None, None) == _lib.HX_EINVAL
+    assert L.hx_read_probe(0x40008, 1024, out, None) == _lib.HX_EINVAL      # misaligned
+    assert L.hx_read_probe(0x40000, 0, out, None) == _lib.HX_EINVAL
+    assert L.hx_read_probe(0x40000, 1000, out, None) == _lib.HX_EINVAL      # not a multiple of 16
+    if not torch.cuda.is_available():
+        assert L.hx_read_probe(0x40000, 1024, out, None) == _lib.HX_EHIP    # valid arguments reach the launch
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")

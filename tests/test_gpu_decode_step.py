@@ -159,3 +159,17 @@ def test_launch_trace_brackets_each_kernel():
         with api.Trace(capacity=1):
             api.decode_step(c, *new, None, None, inp.q, inp.ctx, w.softmax_scale, o, lse, ws)
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("nbytes", [16, 1 << 20, (64 << 20) + 48])
+def test_read_probe_reads_every_byte_once(nbytes):
+    """hx_read_probe: the XOR of its per-workgroup results is the XOR of every
+    32-bit word of the buffer, so every word is read exactly once (a word
+    read twice or skipped changes it for these random words)."""
+    g = torch.Generator().manual_seed(nbytes)
+    words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    want = np.bitwise_xor.reduce(words.numpy().view(np.uint32))
+    out = api.read_probe(words.to(DEV))
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == want
