@@ -133,12 +133,13 @@ def kernel_src_hash(w):
     """Hash of the partial kernel's sources for workload w, to tell whether
     recorded counters still describe the kernel that runs."""
     here = os.path.dirname(os.path.abspath(__file__))
+    shared = ("hx_common.h", "hx_append.h", "hx_quant.h")   # the fused append / quantisation are part of it
     if w.v_alias_k:
-        files = ("decode_mla.hip", "hx_common.h")
+        files = ("decode_mla.hip",) + shared
     elif w.G > 16:
-        files = ("decode_gqa_wide.hip", "hx_gqa_frag.h", "hx_common.h")
+        files = ("decode_gqa_wide.hip", "hx_gqa_frag.h") + shared
     else:
-        files = ("decode_gqa.hip", "hx_gqa_frag.h", "hx_common.h")
+        files = ("decode_gqa.hip", "hx_gqa_frag.h") + shared
     h = hashlib.sha256()
     for p in files:
         with open(os.path.join(here, "long_context_decode_split_amd", "csrc", p), "rb") as f:
@@ -146,11 +147,17 @@ def kernel_src_hash(w):
     return h.hexdigest()[:16]
 
 
-def traffic_key(w, layout):
-    return w.name if layout == "dense" else f"{w.name}+{layout}"
+def traffic_key(w, layout, append="fused"):
+    """Which recorded counters describe this run's partial kernel: one per
+    workload, cache layout and append mode (the fused append and the fused
+    quantisation are other instantiations of the kernel)."""
+    key = w.name if layout == "dense" else f"{w.name}+{layout}"
+    if append == "codes":
+        return key + "+codes"
+    return key + "+bf16append" if append == "bf16" and w.dtype != "bf16" else key
 
 
-def recorded_traffic(w, layout="dense"):
+def recorded_traffic(w, layout="dense", append="fused"):
     """HBM bytes per launch of the partial kernel from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json (scaled by
     a copy of known size), or None when none was recorded for this workload
@@ -158,7 +165,7 @@ def recorded_traffic(w, layout="dense"):
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(traffic_key(w, layout))
+            rec = json.load(f).get(traffic_key(w, layout, append))
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_src_sha16") != kernel_src_hash(w):
@@ -366,7 +373,7 @@ def measure(w, args, steps, warmup, append, attn, layout, cpu_budget, flags=0, f
             "peak": peak_gbs,
             "unit": "GB/s",
             "frac": round(kern_gbs / peak_gbs, 4),
-            "traffic": recorded_traffic(w, layout),
+            "traffic": recorded_traffic(w, layout, append),
             "kernel_avg_us": round(part_ms * 1e3, 2),
             "mfma_tflops": round(flops / (part_ms * 1e-3) / 1e12, 2),
             "mfma_frac": round(flops / (part_ms * 1e-3) / roofline.MFMA_BF16_DENSE_FLOPS, 4),
