@@ -232,8 +232,11 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bl, int g, 
 // Fused decode step: the partial-kernel workgroup of (request bl, KV head g,
 // slice r) that owns the slice's local chunk tiles [c0, c1) first appends the
 // step's new rows that fall in them, then holds every wave at a workgroup
-// barrier (which also waits for the stores) before any tile is read.  The new
-// rows are the newest of the context, so each lies in some workgroup's range.
+// barrier before any tile is read.  The barrier is a workgroup-scope
+// release/acquire, so the workgroup's later reads of the tiles (vector loads
+// or direct global-to-LDS copies, issued from the same CU) see these stores;
+// no other workgroup reads these tiles during the launch.  The new rows are
+// the newest of the context, so each lies in some workgroup's range.
 // Uniform over the workgroup.
 __device__ __forceinline__ void fused_append(const AppendArgs& a, int bl, int g, int r, int64_t c0, int64_t c1) {
   const int64_t pos = a.pos[bl], end = pos + a.count[bl];
