@@ -70,12 +70,17 @@ typedef enum {
 #define HX_CHUNK 16
 
 /* hx_kv_desc.flags.  HX_FLAG_P_BF16: the MLA kernel's value product takes
- * the softmax weights P rounded once to bf16 — about 27% faster at 1M
- * tokens, with an output error of up to 2^-8 times half the range of V
- * (measured up to 2e-3 on N(0, 0.5) data with short slices).  By default P
- * enters as a bf16 high part plus the bf16 of its rounding residual (error
- * about 2^-16 of V's range).  GQA bf16 caches always split P (no measurable
- * cost there); fp8 / MXFP4 caches round it once. */
+ * the softmax weights P rounded once to bf16 everywhere, with an output
+ * error of up to 2^-8 times half the range of V (measured up to 2e-3 on
+ * N(0, 0.5) data with short slices).  By default P enters as a bf16 high
+ * part plus the bf16 of its rounding residual (error about 2^-16 of V's
+ * range) on every 32-token tile where some weight exceeds 2^-10 of its
+ * head's running sum, and rounded once on the others, where each weight is
+ * a tiny share of the total and the rounding errors average out (measured
+ * at 1M tokens: 2,635 us against 3,112 us with the residual everywhere and
+ * ~2,600 us with the flag, all within 4e-6 of the exact output).  GQA bf16
+ * caches always split P (no measurable cost there); fp8 / MXFP4 caches
+ * round it once. */
 #define HX_FLAG_P_BF16 1
 
 /* Describes one KV cache (one layer).  Supported combinations:

@@ -20,7 +20,15 @@
 // rounding residual (SPLITP, the default): rounded once, P's 8 significant
 // bits put the output's error at up to 2^-8 times half the range of V, which
 // for short slices reaches the 2e-3 bound of bf16 caches; the residual's
-// products double the value product's matrix-core work (measured +27%).
+// products double the value product's matrix-core work.  They are what
+// keeps heavy weights exact, so a wave skips them on a tile where every
+// weight of its heads is at most 2^-HX_MLA_RES_LOG2 of that head's running
+// sum (each weight then is at most that fraction of the final sum, and the
+// rounding errors of many such small weights average out instead of adding
+// up); the first tiles of a run, tiles with needles and short slices keep
+// them.  Measured at 2^20 tokens: 2^-12 / 2^-10 / 2^-8 / always skipping
+// took 2,845 / 2,635 / 2,585 / 2,600 us, every output within 4e-6 of the
+// oracle (the residual everywhere: 3,112 us).
 //
 // A tile (two chunk tiles, 36 KiB) is copied from HBM into LDS unchanged with
 // direct global-to-LDS loads (no VGPRs), into one of four buffers: three
@@ -65,6 +73,13 @@ constexpr int kVBlocks = kDv / 32;                 // 32-column value blocks (16
 constexpr int kKPre = 4;                           // score operands read ahead
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kHeadroom = 64.0f;                 // log2 of the largest unnormalised P
+#ifndef HX_MLA_RES_LOG2
+#define HX_MLA_RES_LOG2 10
+#endif
+// a tile's residual products are skipped when each weight is at most
+// 2^-HX_MLA_RES_LOG2 of its head's running sum
+constexpr float pow2i(int e) { return e == 0 ? 1.0f : (e > 0 ? 2.0f * pow2i(e - 1) : 0.5f * pow2i(e + 1)); }
+constexpr float kResFrac = pow2i(-HX_MLA_RES_LOG2);
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -286,6 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   uint32_t pk[8];
   uint32_t pr[8];   // SPLITP: bf16 of the rounding residuals of P, same layout
   float mseen = -INFINITY;   // largest scaled score seen in this run (base 2)
+  bool res = false;          // SPLITP: the tile softmax last ran on needs the residual products (wave-uniform)
   auto softmax = [&](f32x16 sc, int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
     if (valid < kTileTok) {
@@ -299,17 +315,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     cm = max_xor32(cm) * c2;
     mseen = fmaxf(mseen, cm);
     if (mref == -INFINITY) mref = cm;   // first tile of the run (at least one valid token)
+    float p[16];
+    float ps = 0.f, pm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -mref));
+      ps += p[i];
+      pm = fmaxf(pm, p[i]);
+    }
+    lsum += ps;
+    // the lane's running sum covers half of its head's tokens so far, so the
+    // two lanes' sum bounds the head's final sum from below
+    if constexpr (SPLITP) res = __any(pm > kResFrac * sum_xor32(lsum));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i], c2, -mref));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i + 1], c2, -mref));
-      lsum += p0 + p1;
-      const bf16x2 pb2 = {(__bf16)p0, (__bf16)p1};
+      const bf16x2 pb2 = {(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
       pk[i] = __builtin_bit_cast(uint32_t, pb2);
       // the rounded values the matrix product uses, summed for the normalisation
       lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, lsum_mfma, false);
-      if constexpr (SPLITP) {
-        const float r0 = p0 - __uint_as_float(pk[i] << 16), r1 = p1 - __uint_as_float(pk[i] & 0xffff0000u);
+    }
+    if (SPLITP && res) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r0 = p[2 * i] - __uint_as_float(pk[i] << 16);
+        const float r1 = p[2 * i + 1] - __uint_as_float(pk[i] & 0xffff0000u);
         const bf16x2 rb2 = {(__bf16)r0, (__bf16)r1};
         pr[i] = __builtin_bit_cast(uint32_t, rb2);
         lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(rb2, kOnes2, lsum_mfma, false);
@@ -332,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   auto iteration = [&](auto cur_t, auto next_t, int k) -> bool {
     constexpr bool CUR = decltype(cur_t)::value;
     constexpr bool NEXT = decltype(next_t)::value;
+    const bool res_k = SPLITP && CUR && res;   // tile k's softmax asked for the residual products
     const int par = k & 1;
     const bool over = __any(mseen > mref + kHeadroom);   // all lanes vote, outside the lane-0 branch
     if (lane == 0) s_over[par][wave] = over ? 1u : 0u;
@@ -362,17 +392,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
             __builtin_bit_cast(bf16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
         acc[s & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[s % 3]), pb, acc[s & 15],
                                                               0, 0, 0);
-        if constexpr (SPLITP) {   // the residual's products, on the same value fragment
-          const bf16x8 pl =
-              __builtin_bit_cast(bf16x8, make_uint4(pr[4 * u], pr[4 * u + 1], pr[4 * u + 2], pr[4 * u + 3]));
-          acc[s & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[s % 3]), pl,
-                                                                acc[s & 15], 0, 0, 0);
-        }
       }
       if (NEXT) {
         if (s + kKPre < kSteps) kv[(s + kKPre) % (kKPre + 1)] = kread(tk, s + kKPre);
         sc = s == 0 ? mfma_s0(__builtin_bit_cast(bf16x8, kv[0]), qf[0])
                     : mfma_s(__builtin_bit_cast(bf16x8, kv[s % (kKPre + 1)]), qf[s], sc);
+      }
+    }
+    if (res_k) {   // tile k's residual products (uniform branch), its value fragments read again
+      uint4 vr[3];
+      vr[0] = vread(tv, 0);
+      vr[1] = vread(tv, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * kVBlocks; ++i) {
+        if (i + 2 < 2 * kVBlocks) vr[(i + 2) % 3] = vread(tv, i + 2);
+        const int u = i >> 4;
+        const bf16x8 pl =
+            __builtin_bit_cast(bf16x8, make_uint4(pr[4 * u], pr[4 * u + 1], pr[4 * u + 2], pr[4 * u + 3]));
+        acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % 3]), pl, acc[i & 15],
+                                                              0, 0, 0);
       }
     }
     if (NEXT) {
