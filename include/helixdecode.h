@@ -88,7 +88,8 @@ typedef enum {
  *        more than 16 query heads run a kernel that shares each tile pair
  *        among the workgroup's waves through LDS);
  *   MLA: Dk = 576, Dv = 512, v_alias_k = 1 (V is the first 512 columns of
- *        the K row: one latent KV head), dtype HX_KV_BF16, G = 128.
+ *        the K row: one latent KV head), dtype any, G = 128 (fp8 and MXFP4
+ *        rows are converted to bf16 in LDS before the matrix products).
  * Other combinations return HX_EUNSUPPORTED. */
 typedef struct {
   int32_t P;          /* slices (KV-parallel ranks), 1..64 */
@@ -115,7 +116,12 @@ typedef struct {
  * NULL): each [P][B][Hkv][cap/16] chunk tile of 2,176 bytes holds the K
  * codes (1,024 B), the V codes (1,024 B), then the e8m0 exponents of K and
  * of V (16 rows x D/32 bytes each, row-major), so the attention streams one
- * contiguous run per slice. */
+ * contiguous run per slice.
+ * Quantised MLA caches (v_alias_k = 1, fp8 or MXFP4) are one plane too,
+ * passed as k: each chunk tile holds the 16 latent rows' codes, row-major
+ * (fp8: 576 bytes per row; MXFP4: 288 bytes, the even element in the low
+ * nibble), then fp8: the group's float scale padded to 16 bytes (9,232 B
+ * per tile); MXFP4: the rows' e8m0 bytes, 18 per row, row-major (4,896 B). */
 typedef struct {
   void* k;
   void* v;
@@ -127,7 +133,7 @@ typedef struct {
  * pass NULL), and the tile sizes. */
 typedef struct {
   size_t k_bytes, v_bytes, k_scale_bytes, v_scale_bytes;
-  size_t k_tile_bytes, v_tile_bytes; /* bytes of one 16-row chunk tile (MXFP4: the whole packed tile) */
+  size_t k_tile_bytes, v_tile_bytes; /* bytes of one 16-row chunk tile (packed caches: the whole packed tile) */
   int64_t n_max;                     /* largest context: P * cap */
 } hx_kv_layout_info;
 

@@ -54,4 +54,10 @@ MXFP4_RAGGED = Workload("mxfp4_ragged", B=16, Hq=16, Hkv=1, Dk=128, Dv=128, v_al
 WIDE_GQA_G64 = Workload("wide_gqa_g64", B=8, Hq=64, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", P=8,
                         ctx=1 << 20)
 
-ALL = {w.name: w for w in (TINY_GQA, LLAMA405B_SHARE, DEEPSEEK_MLA, FP8_GQA, MXFP4_RAGGED, WIDE_GQA_G64)}
+# The MLA step with quantised latent rows (the review's DeepSeek-R1 results
+# are for FP4): fp8 e4m3 and MXFP4 caches of the same shape.
+DEEPSEEK_MLA_FP8 = DEEPSEEK_MLA.scaled(name="deepseek_r1_mla_fp8", dtype="fp8_e4m3")
+DEEPSEEK_MLA_MXFP4 = DEEPSEEK_MLA.scaled(name="deepseek_r1_mla_mxfp4", dtype="mxfp4")
+
+ALL = {w.name: w for w in (TINY_GQA, LLAMA405B_SHARE, DEEPSEEK_MLA, FP8_GQA, MXFP4_RAGGED, WIDE_GQA_G64,
+                           DEEPSEEK_MLA_FP8, DEEPSEEK_MLA_MXFP4)}

@@ -39,6 +39,15 @@
 // 16-byte rows (score operand) and through ds_read_b64_tr_b16 (transposed
 // value operand), and one stored copy of the latent row serves both.
 //
+// fp8 and MXFP4 latent rows (one plane of packed chunk tiles: 16 rows of
+// codes, row-major, then the group's fp32 scale resp. the rows' e8m0 bytes)
+// are copied unchanged into a two-buffer LDS staging ring and converted by
+// all threads into the bf16 tile layout above (rows past the slice end as
+// zeros), so the products below run as for bf16 rows; three bf16 tile
+// buffers then fit next to the staging ring.  One copy is in flight while
+// the workgroup converts the tile after next and computes the current one.
+// Their P is rounded once (as for the quantised GQA caches).
+//
 // Lane layouts used below (64-lane wave, l = lane, half = l / 32):
 //   32x32x16 A operand: row l % 32, k = 8 * half + j (j = 0..7);
 //   B operand: column l % 32, same k; C/D: register r holds row
@@ -49,6 +58,7 @@
 #include <type_traits>
 
 #include "hx_append.h"
+#include "hx_gqa_frag.h"
 
 namespace hx {
 namespace {
@@ -67,7 +77,19 @@ constexpr int kTileTok = 32;                       // tokens per LDS tile (two c
 constexpr int kRowBytes = kDk * 2;                 // 1152
 constexpr int kTileBytes = kTileTok * kRowBytes;   // 36 KiB
 constexpr int kBlocksPerWave = kTileBytes / 1024 / kWaves;   // 1 KiB copies per wave per tile (9)
-constexpr int kNBuf = 4;                           // tile buffers
+constexpr int kNBuf = 4;                           // tile buffers (bf16 rows)
+// Quantised latent rows: packed chunk tiles of kQChunk bytes (codes, then
+// scales), staged two 32-row tiles at a time, copied in 16-byte pieces of
+// which each wave takes a quarter (kQCopies copy instructions per wave).
+template <int FMT>
+constexpr int kQChunk = FMT == 1 ? 16 * 576 + 16 : 16 * 288 + 16 * 18;   // 9,232 / 4,896 bytes
+template <int FMT>
+constexpr int kQCodes = FMT == 1 ? 16 * 576 : 16 * 288;                  // code bytes of a chunk tile
+template <int FMT>
+constexpr int kQPieces = kQChunk<FMT> / 16;                              // 577 / 306
+template <int FMT>
+constexpr int kQCopies = ((2 * kQPieces<FMT> + 3) / 4 + 63) / 64;        // 5 / 3
+constexpr int kQBuf = 3;                                                 // bf16 tile buffers next to the staging
 constexpr int kSteps = kDk / 16;                   // k-steps of the score product (36)
 constexpr int kVBlocks = kDv / 32;                 // 32-column value blocks (16)
 constexpr int kKPre = 4;                           // score operands read ahead
@@ -110,6 +132,13 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
                : "memory");
 }
 
+// The same copy from a per-lane 64-bit address (lanes may read from two
+// different chunk tiles); inactive lanes copy nothing.
+__device__ __forceinline__ void dma16a(const void* g, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 // Workgroup barrier after this wave's loads down to VMCNT still in flight
 // have landed and all its LDS accesses are done.  The asm is also a compiler
 // memory barrier, so no LDS access moves across it.
@@ -145,10 +174,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-template <bool PAGED, bool SPLITP, bool FUSED>
+template <bool PAGED, bool SPLITP, bool FUSED, int FMT>
 __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
-  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNBuf][kTileBytes];
+  constexpr int kNB = FMT == 0 ? kNBuf : kQBuf;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kNB][kTileBytes];
+  // quantised rows: the staging ring (two 32-row tiles as stored); fp8: the
+  // group scales of the tile in each bf16 buffer (rows 0-15, 16-31)
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[FMT == 0 ? 1 : 2][FMT == 0 ? 16 : 2 * kQChunk<FMT>];
+  __shared__ float s_qscale[kNB][2];
   // 1 when a wave saw a score beyond its headroom; two sets, by the parity of
   // the iteration, so that a wave writing the next flag cannot overtake a
   // slower wave still reading the current ones
@@ -242,6 +276,83 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     }
   };
 
+  const uint8_t* qbase = a.k + (tile0 + cbeg) * a.k_tile;   // dense quantised rows: the split's first chunk tile
+  // ---- quantised rows: copy of tile k's two packed chunk tiles, as stored,
+  //      into staging buffer k % 2.  The 16-byte pieces of the pair are
+  //      numbered chunk 0 first; wave w copies pieces [2 N w / 4, 2 N (w+1)
+  //      / 4) (N pieces per chunk tile), kQCopies instructions of up to 64
+  //      consecutive pieces each, so every wave issues the same number.  A
+  //      pair whose second chunk holds no row of the slice copies its first
+  //      chunk twice (the conversion zeroes those rows).
+  auto stage = [&](int k) {
+    if constexpr (FMT != 0) {
+      constexpr int N = kQPieces<FMT>;
+      const int valid = min(kTileTok, ntok - k * kTileTok);
+      const uint8_t* c0p;
+      const uint8_t* c1p;
+      if constexpr (PAGED) {
+        c0p = src0;
+        c1p = src1;
+      } else {
+        c0p = qbase + (int64_t)(2 * k) * a.k_tile;
+        c1p = valid > kChunk ? c0p + a.k_tile : c0p;
+      }
+      uint8_t* dst = &s_stage[k & 1][0];
+      const int pbeg = 2 * N * wave / kWaves, pend = 2 * N * (wave + 1) / kWaves;
+#pragma unroll
+      for (int i = 0; i < kQCopies<FMT>; ++i) {
+        const int first = pbeg + 64 * i;
+        const int pc = first + lane;
+        if (pc < pend) dma16a(pc < N ? c0p + 16 * pc : c1p + 16 * (pc - N), lds_addr(dst + 16 * first));
+      }
+    }
+  };
+  // ---- quantised rows: staging buffer of tile k -> bf16 buffer k % kNB in
+  //      the bf16 tile layout (row m's 16-byte piece q at piece position
+  //      q ^ mla_swz(m)); rows at or past the slice end become zeros.  fp8:
+  //      the codes (e4m3 values are bf16 values), the two group scales kept
+  //      in s_qscale for the softmax, which folds them into the scores and
+  //      into P; MXFP4: e2m1 x 2^(E-127), exact in bf16.  Each thread
+  //      converts 9 of the tile's 32 x 72 pieces of 8 elements.
+  auto convert = [&](int k) {
+    if constexpr (FMT != 0) {
+      const lds_u8* st = (const lds_u8*)&s_stage[k & 1][0];
+      lds_u8* dt = (lds_u8*)&s_tile[k % kNB][0];
+      const int valid = min(kTileTok, ntok - k * kTileTok);
+      constexpr int kItems = kTileTok * (kDk / 8);   // 2,304
+      // one piece at a time: the accumulators and Q fragments leave few registers
+#pragma unroll 1
+      for (int j = 0; j < kItems / kThreads; ++j) {
+        const int i = threadIdx.x + kThreads * j;
+        const int m = i / (kDk / 8), q = i - m * (kDk / 8);
+        const lds_u8* cb = st + (m >> 4) * kQChunk<FMT>;   // the row's chunk tile
+        const int mr = m & 15;
+        uint4 out = make_uint4(0u, 0u, 0u, 0u);
+        if (m < valid) {
+          if constexpr (FMT == 1) {
+            const uint2 c8 = *(const __attribute__((address_space(3))) uint2*)(cb + mr * kDk + 8 * q);
+            out = make_uint4(frag::fp8x2_to_bf16x2<false>(c8.x), frag::fp8x2_to_bf16x2<true>(c8.x),
+                             frag::fp8x2_to_bf16x2<false>(c8.y), frag::fp8x2_to_bf16x2<true>(c8.y));
+          } else {
+            const uint32_t c4 = *(const __attribute__((address_space(3))) uint32_t*)(cb + mr * (kDk / 2) + 4 * q);
+            const uint32_t e = cb[kQCodes<FMT> + mr * (kDk / 32) + (q >> 2)];
+            const float sc = __uint_as_float(e << 23);   // 2^(E-127); E = 0 reads as 0, E = 255 as +inf
+            out = make_uint4(frag::fp4x2_to_bf16x2<0>(c4, sc), frag::fp4x2_to_bf16x2<1>(c4, sc),
+                             frag::fp4x2_to_bf16x2<2>(c4, sc), frag::fp4x2_to_bf16x2<3>(c4, sc));
+          }
+        }
+        *(lds_u4*)(dt + m * kRowBytes + 16 * (q ^ mla_swz(m))) = out;
+      }
+      if constexpr (FMT == 1) {   // a group with no row of the slice: scale 1 (its rows are zeros)
+        if (threadIdx.x < 2)
+          s_qscale[k % kNB][threadIdx.x] =
+              16 * (int)threadIdx.x < valid
+                  ? *(const __attribute__((address_space(3))) float*)(st + threadIdx.x * kQChunk<FMT> + kQCodes<FMT>)
+                  : 1.0f;
+      }
+    }
+  };
+
   f32x16 acc[kVBlocks];
 #pragma unroll
   for (int i = 0; i < kVBlocks; ++i) acc[i] = f32x16{};
@@ -304,6 +415,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   bool res = false;          // SPLITP: the tile softmax last ran on needs the residual products (wave-uniform)
   auto softmax = [&](f32x16 sc, int k) {
     const int valid = min(kTileTok, ntok - k * kTileTok);
+    // fp8 rows: the group scale of rows 0-15 (registers 0-7) and 16-31 (8-15)
+    float gs[2] = {1.0f, 1.0f};
+    if constexpr (FMT == 1) {
+      gs[0] = s_qscale[k % kNB][0];
+      gs[1] = s_qscale[k % kNB][1];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] *= gs[i >> 3];
+    }
     if (valid < kTileTok) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -327,12 +446,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     // the lane's running sum covers half of its head's tokens so far, so the
     // two lanes' sum bounds the head's final sum from below
     if constexpr (SPLITP) res = __any(pm > kResFrac * sum_xor32(lsum));
+    if constexpr (FMT == 1) {
+      // fp8 rows: each group's scale folded into its weights, the rounded
+      // products divided by it normalise O (a zero scale: the weights
+      // unrounded, the values being 0)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x2 pb2 = {(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
-      pk[i] = __builtin_bit_cast(uint32_t, pb2);
-      // the rounded values the matrix product uses, summed for the normalisation
-      lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, lsum_mfma, false);
+      for (int grp = 0; grp < 2; ++grp) {
+        float rs = 0.f, ps2 = 0.f;
+#pragma unroll
+        for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
+          const bf16x2 pb2 = {(__bf16)(p[2 * i] * gs[grp]), (__bf16)(p[2 * i + 1] * gs[grp])};
+          pk[i] = __builtin_bit_cast(uint32_t, pb2);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, rs, false);
+          ps2 += p[2 * i] + p[2 * i + 1];
+        }
+        lsum_mfma += gs[grp] != 0.f ? rs / gs[grp] : ps2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x2 pb2 = {(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
+        pk[i] = __builtin_bit_cast(uint32_t, pb2);
+        // the rounded values the matrix product uses, summed for the normalisation
+        lsum_mfma = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, lsum_mfma, false);
+      }
     }
     if (SPLITP && res) {
 #pragma unroll
@@ -365,13 +502,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     const int par = k & 1;
     const bool over = __any(mseen > mref + kHeadroom);   // all lanes vote, outside the lane-0 branch
     if (lane == 0) s_over[par][wave] = over ? 1u : 0u;
-    if (CUR && k + 3 < ntiles) prep(k + 3);   // pool lookups complete in the barrier's wait
-    if (k + 2 < ntiles) wait_barrier<kBlocksPerWave>();
-    else wait_barrier<0>();
+    if constexpr (FMT == 0) {
+      if (CUR && k + 3 < ntiles) prep(k + 3);   // pool lookups complete in the barrier's wait
+      if (k + 2 < ntiles) wait_barrier<kBlocksPerWave>();
+      else wait_barrier<0>();
+    } else {
+      // quantised rows: the barrier publishes tile k + 1's conversion and
+      // tile k + 2's staging copy (the only copy in flight)
+      if (k + 3 < ntiles) prep(k + 3);
+      wait_barrier<0>();
+    }
     if ((s_over[par][0] | s_over[par][1] | s_over[par][2] | s_over[par][3]) != 0) return true;
-    if (CUR && k + 3 < ntiles) load_tile(k + 3);
-    const lds_u8* tv = (const lds_u8*)&s_tile[(k + kNBuf) % kNBuf][0];
-    const lds_u8* tk = (const lds_u8*)&s_tile[(k + 1) % kNBuf][0];
+    if constexpr (FMT == 0) {
+      if (CUR && k + 3 < ntiles) load_tile(k + 3);
+    } else {
+      if (k + 3 < ntiles) stage(k + 3);    // into the staging buffer tile k + 1 left
+      if (k + 2 < ntiles) convert(k + 2);  // into the bf16 buffer tile k - 1 left
+    }
+    const lds_u8* tv = (const lds_u8*)&s_tile[(k + kNB) % kNB][0];
+    const lds_u8* tk = (const lds_u8*)&s_tile[(k + 1) % kNB][0];
     f32x16 sc;
     uint4 kv[kKPre + 1];
     uint4 vv[3];
@@ -423,12 +572,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   typedef std::integral_constant<bool, false> F;
 
   for (;;) {
+    if constexpr (FMT == 0) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < ntiles) {
-        prep(j);
-        load_tile(j);
-      }
+      for (int j = 0; j < 3; ++j)
+        if (j < ntiles) {
+          prep(j);
+          load_tile(j);
+        }
+    } else {
+      // stage tiles 0 and 1, convert tile 0 once its copy has landed
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j < ntiles) {
+          prep(j);
+          stage(j);
+        }
+      if (ntiles > 1) wait_barrier<kQCopies<FMT>>();
+      else wait_barrier<0>();
+      if (ntiles > 0) convert(0);
+    }
     bool restart = ntiles > 0 && iteration(F{}, T{}, -1);
     for (int k = 0; !restart && k + 1 < ntiles; ++k) restart = iteration(T{}, T{}, k);
     if (!restart && ntiles > 0) restart = iteration(T{}, F{}, ntiles - 1);
@@ -474,20 +636,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
 
 }  // namespace
 
-hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st) {
+hipError_t launch_mla_partial(const PartialArgs& a, int dtype, hipStream_t st) {
   const int nwg = a.wg_begin[a.nb];
   if (nwg == 0) return hipSuccess;
   const dim3 grid(nwg), block(kThreads);
+  if (dtype != HX_KV_BF16) {
+    // quantised rows: P rounded once, the step's rows appended beforehand
+    if (a.fused_append) return hipErrorInvalidValue;
+    const bool paged = a.table != nullptr;
+    if (dtype == HX_KV_FP8_E4M3) {
+      if (paged) hipLaunchKernelGGL((mla_partial_kernel<true, false, false, 1>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((mla_partial_kernel<false, false, false, 1>), grid, block, 0, st, a);
+    } else {
+      if (paged) hipLaunchKernelGGL((mla_partial_kernel<true, false, false, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((mla_partial_kernel<false, false, false, 2>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   const int v = (a.table ? 4 : 0) | (a.split_p ? 2 : 0) | (a.fused_append == 1 ? 1 : 0);
   switch (v) {
-    case 0: hipLaunchKernelGGL((mla_partial_kernel<false, false, false>), grid, block, 0, st, a); break;
-    case 1: hipLaunchKernelGGL((mla_partial_kernel<false, false, true>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((mla_partial_kernel<false, true, false>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((mla_partial_kernel<false, true, true>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((mla_partial_kernel<true, false, false>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((mla_partial_kernel<true, false, true>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((mla_partial_kernel<true, true, false>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((mla_partial_kernel<true, true, true>), grid, block, 0, st, a); break;
+    case 0: hipLaunchKernelGGL((mla_partial_kernel<false, false, false, 0>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((mla_partial_kernel<false, false, true, 0>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((mla_partial_kernel<false, true, false, 0>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((mla_partial_kernel<false, true, true, 0>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((mla_partial_kernel<true, false, false, 0>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((mla_partial_kernel<true, false, true, 0>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((mla_partial_kernel<true, true, false, 0>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((mla_partial_kernel<true, true, true, 0>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }

@@ -100,8 +100,11 @@ static hx_status plane_refs(const hx_kv_desc& d, const Geometry& g, const hx_kv_
   if (!c->k) return fail(HX_EINVAL, "null K plane");
   if (g.packed) {
     if (c->v || c->k_scale || c->v_scale)
-      return fail(HX_EINVAL, "an MXFP4 cache is one plane: pass it as k and leave v, k_scale and v_scale NULL");
-    const int64_t off[4] = {0, g.k_tile, g.k_tile + g.v_tile, g.k_tile + g.v_tile + g.ks_tile};
+      return fail(HX_EINVAL, "a packed cache (MXFP4, or a quantised MLA cache) is one plane: pass it as k and leave "
+                  "v, k_scale and v_scale NULL");
+    // aliased (MLA): V codes and scales are the K ones
+    const int64_t off[4] = {0, d.v_alias_k ? 0 : g.k_tile, g.k_tile + g.v_tile,
+                            d.v_alias_k ? g.k_tile : g.k_tile + g.v_tile + g.ks_tile};
     for (int i = 0; i < 4; ++i) {
       p.base[i] = (uint8_t*)c->k + off[i];
       p.stride[i] = g.packed_tile;
@@ -151,10 +154,28 @@ hx_status geometry(const hx_kv_desc& d, Geometry* g) {
       t.packed = true;
       t.packed_tile = t.k_tile + t.v_tile + t.ks_tile + t.vs_tile;   // 2,176 B
     }
-  } else if (d.Dk == 576 && d.Dv == 512 && d.v_alias_k && d.dtype == HX_KV_BF16) {
+  } else if (d.Dk == 576 && d.Dv == 512 && d.v_alias_k) {
     t.kind = 1;
-    t.lay_k = kLayMlaBf16; t.lay_v = -1; t.ebits = 16;
-    t.k_tile = (int64_t)kChunk * 576 * 2; t.v_tile = 0; t.ks_tile = t.vs_tile = 0;
+    t.lay_v = -1;
+    t.v_tile = 0;
+    t.vs_tile = 0;
+    if (d.dtype == HX_KV_BF16) {
+      t.lay_k = kLayMlaBf16; t.ebits = 16;
+      t.k_tile = (int64_t)kChunk * 576 * 2; t.ks_tile = 0;
+    } else {
+      // quantised latent rows: one plane of packed tiles, the codes (row-major)
+      // then the scales, so a workgroup streams one contiguous run; fp8: the
+      // group's fp32 scale padded to 16 bytes; MXFP4: 16 rows x 18 e8m0 bytes
+      t.packed = true;
+      if (d.dtype == HX_KV_FP8_E4M3) {
+        t.lay_k = kLayRowU8; t.ebits = 8;
+        t.k_tile = (int64_t)kChunk * 576; t.ks_tile = 16;
+      } else {
+        t.lay_k = kLayRowU4; t.ebits = 4;
+        t.k_tile = (int64_t)kChunk * 576 / 2; t.ks_tile = (int64_t)kChunk * (576 / 32);
+      }
+      t.packed_tile = t.k_tile + t.ks_tile;   // 9,232 B (fp8), 4,896 B (MXFP4)
+    }
   } else {
     return fail(HX_EUNSUPPORTED, "unsupported cache: Dk=%d Dv=%d v_alias_k=%d dtype=%d", d.Dk, d.Dv, d.v_alias_k,
                 d.dtype);
@@ -445,12 +466,13 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
   const hx_kv_desc& d = *desc;
   if (d.dtype == HX_KV_BF16) return kv_append(desc, cache, pool, k_new, v_new, nullptr, nullptr, pos, count, n_new, stream);
   if (n_new < 1) return fail(HX_EINVAL, "n_new=%d must be >= 1", n_new);
-  // quantised caches are GQA caches (Dk = Dv = 128, separate V)
   PlaneRefs pr;
   s = plane_refs(d, g, cache, &pr);
   if (s) return s;
-  if (!k_new || !v_new) return fail(HX_EINVAL, "null k_new or v_new");
-  if (!aligned16(k_new) || !aligned16(v_new)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
+  const bool alias = d.v_alias_k;   // MLA latent rows: K only
+  if (!k_new || (!alias && !v_new)) return fail(HX_EINVAL, "null k_new or v_new");
+  if (alias && v_new) return fail(HX_EINVAL, "v_new must be NULL when v_alias_k = 1");
+  if (!aligned16(k_new) || (v_new && !aligned16(v_new))) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   const int64_t nmax = (int64_t)d.P * d.cap;
   for (int b = 0; b < d.B; ++b) {
     const int32_t cnt = count ? count[b] : n_new;
@@ -466,6 +488,7 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
   a.sc[1] = pr.base[3];
   a.lay[0] = g.lay_k;
   a.lay[1] = g.lay_v;
+  a.nplanes = alias ? 1 : 2;
   a.dtype = d.dtype;
   a.D = d.Dk;
   a.P = d.P;
@@ -492,7 +515,7 @@ static hx_status kv_append_bf16(const hx_kv_desc* desc, const hx_kv_cache* cache
     a.b0 = b0;
     const int64_t off = (int64_t)b0 * d.Hkv * n_new * d.Dk;
     a.src[0] = (const uint16_t*)k_new + off;
-    a.src[1] = (const uint16_t*)v_new + off;
+    a.src[1] = alias ? nullptr : (const uint16_t*)v_new + off;
     s = check_hip(launch_quant_append(a, nb, (hipStream_t)stream), "kv_append_bf16 launch");
     if (s) return s;
     trace_mark("quant_append", (hipStream_t)stream);
@@ -790,7 +813,7 @@ static hx_status decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, P
     a.nb = nb;
     a.fused_append = fuse ? (fuse->quant ? 2 : 1) : 0;
     if (fuse) a.app = append_batch(*fuse, fuse_pos, nullptr, b0, nb);
-    hipError_t e = geo.kind == 1         ? launch_mla_partial(a, (hipStream_t)stream)
+    hipError_t e = geo.kind == 1         ? launch_mla_partial(a, d.dtype, (hipStream_t)stream)
                    : G > kGqaNarrowMaxHeads ? launch_gqa_wide(a, d.dtype, (hipStream_t)stream)
                                             : launch_gqa_partial(a, d.dtype, (hipStream_t)stream);
     s = check_hip(e, "decode_attn_partial launch");
@@ -924,7 +947,9 @@ static hx_status fused_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   hx_status s = append_setup(desc, cache, pool, k_new, v_new, k_scale_new, v_scale_new, pos.data(), nullptr, n_new,
                              &base);
   if (s) return s;
-  if (desc->dtype == HX_KV_MXFP4) {   // no fused kernel for MXFP4 (see decode_gqa.hip): append, then attend
+  // no fused append for MXFP4 codes (see decode_gqa.hip) nor quantised MLA
+  // caches (their kernel converts tiles before reading them): append, then attend
+  if (desc->dtype == HX_KV_MXFP4 || (desc->v_alias_k && desc->dtype != HX_KV_BF16)) {
     // every argument of the attention is checked before the append writes the
     // cache, so a call that fails leaves the cache unchanged
     s = decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse, nullptr,
@@ -948,6 +973,24 @@ static hx_status quant_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   if (desc->dtype == HX_KV_BF16)
     return fused_step(desc, cache, pool, k_new, v_new, nullptr, nullptr, n_new, q, Hq, ctx_len, scale, o, lse, ws,
                       ws_bytes, stream);
+  if (desc->v_alias_k) {
+    // quantised MLA caches: the quantising append kernel, then the attention
+    // (every argument of the attention is checked before the cache is written)
+    if (desc->B < 1) return fail(HX_EINVAL, "B=%d must be >= 1", desc->B);
+    std::vector<int64_t> pos((size_t)desc->B);
+    for (int b = 0; b < desc->B; ++b) {
+      if (ctx_len[b] < n_new)
+        return fail(HX_EINVAL, "ctx_len[%d]=%lld is shorter than the n_new=%d new rows", b, (long long)ctx_len[b],
+                    n_new);
+      pos[(size_t)b] = ctx_len[b] - n_new;
+    }
+    hx_status s = decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o,
+                              lse, nullptr, nullptr, true);
+    if (s) return s;
+    s = kv_append_bf16(desc, cache, pool, k_new, v_new, pos.data(), nullptr, n_new, stream);
+    if (s) return s;
+    return decode_step(desc, cache, pool, q, Hq, ctx_len, scale, nullptr, nullptr, ws, ws_bytes, stream, o, lse);
+  }
   Geometry g;
   hx_status s = geometry(*desc, &g);
   if (s) return s;
@@ -956,7 +999,7 @@ static hx_status quant_step(const hx_kv_desc* desc, const hx_kv_cache* cache, Po
   PlaneRefs pr;
   s = plane_refs(d, g, cache, &pr);
   if (s) return s;
-  // quantised caches are GQA caches (Dk = Dv = 128, separate V)
+  // here quantised GQA caches (Dk = Dv = 128, separate V); MLA rows took the branch above
   if (!k_new || !v_new) return fail(HX_EINVAL, "null k_new or v_new");
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(HX_EINVAL, "device pointers must be 16-byte aligned");
   std::vector<int64_t> pos((size_t)d.B);

@@ -268,7 +268,7 @@ __device__ __forceinline__ void fused_quant(const AppendArgs& a, int bl, int g, 
   for (int64_t c = first; c <= cl; c += a.P) mine |= c / a.P >= c0 && c / a.P < c1;
   if (!mine) return;
   __shared__ float s_red[16];
-  __shared__ uint8_t s_e[kChunk][4];
+  __shared__ uint8_t s_e[kChunk * (128 / 32)];   // GQA rows: 4 exponent blocks each
   const int D = a.width[0];
   for (int64_t c = first; c <= cl; c += a.P) {
     if (c / a.P < c0 || c / a.P >= c1) continue;

@@ -15,6 +15,7 @@ struct QAppendArgs {
   uint8_t* dst[2];         // code planes
   uint8_t* sc[2];          // scale planes
   int lay[2];              // tile layouts
+  int nplanes;             // 2 (K, V), or 1 when V aliases K
   int dtype;               // HX_KV_FP8_E4M3 or HX_KV_MXFP4
   int D;
   int P, B, Hkv;

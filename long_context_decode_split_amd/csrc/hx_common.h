@@ -44,7 +44,8 @@ enum Layout : int {
   kLayGqaFp8K = 2, kLayGqaFp8V = 3,
   kLayGqaFp4K = 4, kLayGqaFp4V = 5,
   kLayMlaBf16 = 6,   // bf16 latent rows, 16-byte pieces XOR-swizzled inside each aligned group of 8
-  kLayRowU8 = 7,     // plain row-major bytes (MXFP4 e8m0 scale rows)
+  kLayRowU8 = 7,     // plain row-major bytes (MXFP4 e8m0 scale rows, fp8 MLA latent rows)
+  kLayRowU4 = 8,     // plain row-major 4-bit elements, the even one in the low nibble (MXFP4 MLA latent rows)
 };
 
 // MLA latent rows (1152 B = 72 pieces of 16 B): piece p of row m is stored at
@@ -132,6 +133,8 @@ HXHD int64_t tile_off2(int lay, int width, int m, int d) {
       const int p = (d >> 3) ^ mla_swz(m);
       return 2 * ((int64_t)m * width * 2 + p * 16 + (d & 7) * 2);
     }
+    case kLayRowU4:
+      return (int64_t)m * width + d;
     case kLayRowU8:
     default:
       return 2 * ((int64_t)m * width + d);
@@ -188,6 +191,12 @@ HXHD void tile_inv(int lay, int width, int64_t off2, int* m, int* d) {
       *d = p * 8 + ((b & 15) >> 1);
       return;
     }
+    case kLayRowU4: {
+      const int64_t e = off2;   // element index: two per byte
+      *m = (int)(e / width);
+      *d = (int)(e % width);
+      return;
+    }
     case kLayRowU8:
     default:
       *m = b / width;
@@ -216,6 +225,10 @@ HXHD void piece_rows(int lay, int width, int64_t byte0, int nbytes, int* mlo, in
     }
     case kLayMlaBf16:     // pieces never straddle a 1,152-byte row
       *mlo = *mhi = b / (width * 2);
+      return;
+    case kLayRowU4:       // row-major nibbles
+      *mlo = 2 * b / width;
+      *mhi = (2 * (b + nbytes) - 1) / width;
       return;
     default:              // row-major bytes
       *mlo = b / width;
@@ -249,7 +262,7 @@ HXHD int64_t tile_of(const TileMap& m, int r, int b, int g, int64_t c) {
 
 // ---------------------------------------------------------------- cache geometry
 struct Geometry {
-  int kind;            // 0 GQA (Dk = Dv = 128), 1 MLA (576 / 512, aliased, bf16)
+  int kind;            // 0 GQA (Dk = Dv = 128), 1 MLA (576 / 512, aliased)
   int lay_k, lay_v;    // tile layouts of the K and V code planes
   int ebits;           // bits per code element: 16, 8 or 4
   int64_t k_tile, v_tile;          // code bytes per chunk tile
@@ -335,7 +348,9 @@ hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
 constexpr int kGqaNarrowMaxHeads = 16;
 constexpr int kGqaWideMaxHeads = 128;
 hipError_t launch_gqa_wide(const PartialArgs& a, int dtype, hipStream_t st);
-hipError_t launch_mla_partial(const PartialArgs& a, hipStream_t st);
+// dtype: the latent rows' format (bf16 tiles are read as stored; fp8 and
+// MXFP4 tiles are converted to bf16 in LDS first)
+hipError_t launch_mla_partial(const PartialArgs& a, int dtype, hipStream_t st);
 // Folds the split records of every slice with more than one split into the
 // slice outputs (o_part, lse_part); no-op when every slice has one split.
 hipError_t launch_split_fold(const PartialArgs& a, hipStream_t st);

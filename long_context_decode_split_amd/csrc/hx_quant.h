@@ -100,11 +100,14 @@ __device__ __forceinline__ float block_max(float v, float* s_red, int tid, int n
 
 }  // namespace quant
 
+// 32-element blocks per row of the widest quantised row (576-wide MLA latent rows).
+constexpr int kQuantMaxBlocks = 576 / 32;
+
 // Quantises the new rows of one tile (fp8: one K or V tile and its scale;
 // MXFP4: one K or V code tile and its row exponents).  Called by all nthr
 // threads of a workgroup (nthr a multiple of 64, at most 1024), uniformly;
-// s_red: nthr / 64 floats of LDS, s_e: 16 x 4 bytes of LDS.
-__device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr, float* s_red, uint8_t (*s_e)[4]) {
+// s_red: nthr / 64 floats of LDS, s_e: 16 x kQuantMaxBlocks bytes of LDS.
+__device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr, float* s_red, uint8_t* s_e) {
   using namespace quant;
   const int D = j.D, lay = j.lay;
   if (j.dtype == HX_KV_FP8_E4M3) {
@@ -128,7 +131,7 @@ __device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr,
       reencode = m_old > 0.f;
     }
     const float ratio = s_old / scale;
-    // each thread owns 8-byte pieces of the 2 KiB tile
+    // each thread owns 8-byte pieces of the code tile (16 x D bytes)
     for (int64_t byte0 = (int64_t)tid * 8; byte0 < kChunk * D; byte0 += (int64_t)nthr * 8) {
       uint2 w = *reinterpret_cast<const uint2*>(j.tile + byte0);
       uint8_t* wb = reinterpret_cast<uint8_t*>(&w);
@@ -161,12 +164,12 @@ __device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr,
         for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(bf16_to_f32(j.src[(int64_t)m * D + 32 * jb + k])));
         int e = amax > 0.f ? floor_log2(amax) - 2 : -127;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        s_e[m][jb] = (uint8_t)(e + 127);
+        s_e[m * nblk + jb] = (uint8_t)(e + 127);
         j.sc[m * nblk + jb] = (uint8_t)(e + 127);
       }
     }
     __syncthreads();
-    // each thread owns 4-byte pieces of the 1 KiB tile
+    // each thread owns 4-byte pieces of the code tile (16 x D / 2 bytes)
     for (int64_t byte0 = (int64_t)tid * 4; byte0 < kChunk * D / 2; byte0 += (int64_t)nthr * 4) {
       uint32_t w = *reinterpret_cast<const uint32_t*>(j.tile + byte0);
       bool touched = false;
@@ -175,7 +178,7 @@ __device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr,
         int m, d;
         tile_inv(lay, D, 2 * byte0 + n, &m, &d);
         if (m >= j.m_lo && m < j.m_hi) {
-          const float y = ldexpf(bf16_to_f32(j.src[(int64_t)m * D + d]), 127 - (int)s_e[m][d >> 5]);
+          const float y = ldexpf(bf16_to_f32(j.src[(int64_t)m * D + d]), 127 - (int)s_e[m * nblk + (d >> 5)]);
           const uint32_t code = encode_e2m1(y);
           w = (w & ~(0xFu << (4 * n))) | (code << (4 * n));
           touched = true;

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a, int64
     const uint16_t bits = *reinterpret_cast<const uint16_t*>(tp + (off2 >> 1));
     val = __uint_as_float((uint32_t)bits << 16);
   } else if (a.dtype == HX_KV_FP8_E4M3) {
-    const float s = reinterpret_cast<const float*>(from_k ? a.ks : a.vs)[tile];
+    const float s = *reinterpret_cast<const float*>((from_k ? a.ks : a.vs) + tile * (from_k ? a.ks_tile : a.vs_tile));
     val = fp8_to_f32(tp[off2 >> 1]) * s;   // one fp32 rounding
   } else {
     const uint8_t byte = tp[off2 >> 1];

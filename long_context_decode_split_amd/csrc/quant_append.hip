@@ -2,7 +2,8 @@
 // written round-robin as produced: Helix summary, paragraph on Helix's two
 // layouts) encoded on the device into fp8 e4m3 or MXFP4 chunk tiles.
 //
-// One workgroup owns one (request, KV head, chunk, K or V) tile, so the
+// One workgroup owns one (request, KV head, chunk, K or V) tile (K only when
+// V aliases K, as in MLA latent rows), so the
 // per-chunk fp8 scale, the re-encoding of stored codes when it grows, and
 // the bytes of rows that share a 16-byte piece with new rows are all handled
 // inside one workgroup (quant_tile in hx_quant.h, which states the rules).
@@ -17,10 +18,10 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(const QAppendArgs a) {
   __shared__ float s_red[kThreads / 64];
-  __shared__ uint8_t s_e[kChunk][4];   // MXFP4 exponents of the new rows (D / 32 = 4 blocks)
+  __shared__ uint8_t s_e[kChunk * kQuantMaxBlocks];   // MXFP4 exponents of the new rows
   int t = blockIdx.x;
-  const int plane = t & 1;
-  t >>= 1;
+  const int plane = t % a.nplanes;   // K, then V (none when V aliases K)
+  t /= a.nplanes;
   const int ci = t % a.max_chunks;
   t /= a.max_chunks;
   const int g = t % a.Hkv;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(const QAppendArg
 }  // namespace
 
 hipError_t launch_quant_append(const QAppendArgs& a, int nb, hipStream_t st) {
-  const int64_t wgs = (int64_t)nb * a.Hkv * a.max_chunks * 2;
+  const int64_t wgs = (int64_t)nb * a.Hkv * a.max_chunks * a.nplanes;
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_append_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, st, a);
   return hipGetLastError();

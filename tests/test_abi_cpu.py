@@ -87,7 +87,14 @@ DESCS = [
     api.KVDesc(P=8, B=3, Hkv=2, Dk=128, Dv=128, v_alias_k=False, dtype="fp8_e4m3", cap=32),
     api.KVDesc(P=8, B=1, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="mxfp4", cap=48),
     api.KVDesc(P=2, B=1, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="bf16", cap=16),
+    api.KVDesc(P=2, B=2, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="fp8_e4m3", cap=32),
+    api.KVDesc(P=4, B=1, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype="mxfp4", cap=16),
 ]
+
+
+def _packed(desc):
+    """One plane of packed tiles: GQA MXFP4, and quantised MLA latent rows."""
+    return desc.dtype == "mxfp4" or (desc.v_alias_k and desc.dtype != "bf16")
 
 
 @pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.dtype}-{d.Dk}")
@@ -97,10 +104,14 @@ def test_layout_sizes(desc):
     bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
     codes = 16 * desc.Dk * bits // 8
     assert lay["n_max"] == desc.P * desc.cap
-    if desc.dtype == "mxfp4":
-        # one plane: each tile holds K codes, V codes, K e8m0, V e8m0
-        assert lay["k_tile_bytes"] == 2 * codes + 2 * 16 * desc.Dk // 32 == 2176
-        assert lay["k_bytes"] == tiles * 2176
+    if _packed(desc):
+        # one plane: GQA MXFP4 tiles hold K codes, V codes, K e8m0, V e8m0; MLA
+        # tiles the latent codes, then the fp32 group scale padded to 16 bytes
+        # (fp8) or the rows' e8m0 bytes (MXFP4)
+        want = {("mxfp4", 128): 2 * codes + 2 * 16 * desc.Dk // 32, ("fp8_e4m3", 576): codes + 16,
+                ("mxfp4", 576): codes + 16 * desc.Dk // 32}[(desc.dtype, desc.Dk)]
+        assert lay["k_tile_bytes"] == want in (2176, 9232, 4896)
+        assert lay["k_bytes"] == tiles * want
         assert lay["v_bytes"] == lay["k_scale_bytes"] == lay["v_scale_bytes"] == lay["v_tile_bytes"] == 0
         return
     assert lay["k_tile_bytes"] == codes
@@ -120,7 +131,7 @@ def test_tile_layout_is_a_bijection(desc):
     lay = api.kv_layout(desc)
     bits = {"bf16": 16, "fp8_e4m3": 8, "mxfp4": 4}[desc.dtype]
     unit = {16: 4, 8: 2, 4: 1}[bits]            # off2 units per element
-    packed = desc.dtype == "mxfp4"
+    packed = _packed(desc)
     for which, width in ((0, desc.Dk), (1, desc.Dv)):
         if which == 1 and desc.v_alias_k:
             continue
@@ -133,15 +144,18 @@ def test_tile_layout_is_a_bijection(desc):
         codes = 16 * width * bits // 8
         lo = codes * 8 // bits if packed and which == 1 else 0    # packed: V codes follow K codes
         assert offs == set(range(lo, lo + codes * 8 // bits)), "elements must fill their part of the tile once"
-    if packed:
+    if packed and desc.dtype == "fp8_e4m3":   # MLA: the group scale right after the codes, for every element
+        assert {api.kv_tile_offset(desc, 2, m, d) for m in (0, 7, 15) for d in (0, 300, 575)} == {2 * 16 * desc.Dk}
+    elif packed:
         scale_bytes = set()
-        for which in (2, 3):
+        for which in ((2,) if desc.v_alias_k else (2, 3)):
             for m in range(16):
                 for d in range(0, desc.Dk, 32):
                     o2 = api.kv_tile_offset(desc, which, m, d)
                     assert o2 % 2 == 0 and api.kv_tile_offset(desc, which, m, d + 31) == o2
                     scale_bytes.add(o2 // 2)
-        assert scale_bytes == set(range(2048, lay["k_tile_bytes"])), "K then V e8m0 bytes end the tile"
+        first = 16 * desc.Dk // 2 * (1 if desc.v_alias_k else 2)
+        assert scale_bytes == set(range(first, lay["k_tile_bytes"])), "the e8m0 bytes end the tile"
 
 
 def test_gqa_bf16_tile_gives_lane_fragments():
@@ -172,7 +186,7 @@ def test_tile_offset_errors():
     (dict(cap=0), _lib.HX_EINVAL), (dict(B=0), _lib.HX_EINVAL), (dict(Dk=64, Dv=64), _lib.HX_EUNSUPPORTED),
     (dict(flags=2), _lib.HX_EINVAL), (dict(flags=-1), _lib.HX_EINVAL),
     (dict(Dk=576, Dv=512, v_alias_k=False), _lib.HX_EUNSUPPORTED),
-    (dict(Dk=576, Dv=512, v_alias_k=True, dtype="fp8_e4m3"), _lib.HX_EUNSUPPORTED),
+    (dict(Dk=576, Dv=256, v_alias_k=True, dtype="fp8_e4m3"), _lib.HX_EUNSUPPORTED),
 ])
 def test_desc_errors(bad, status):
     base = dict(P=4, B=1, Hkv=1, Dk=128, Dv=128, v_alias_k=False, dtype="bf16", cap=64)

@@ -35,11 +35,16 @@ CASES = [
     (configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(40, 9000)), 17, "paged"),
     (configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(40, 9000)), 1, "paged"),
     (configs.FP8_GQA.scaled(B=3, ctx=None, ctx_range=(40, 9000)), 17, "paged"),
+    # quantised MLA caches: the append kernel inside the call, then the attention
+    (configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(40, 3000), P=4, dtype="fp8_e4m3"), 2, "dense"),
+    (configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(40, 3000), P=4, dtype="fp8_e4m3"), 1, "paged"),
+    (configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(40, 3000), P=4, dtype="mxfp4"), 3, "dense"),
+    (configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(40, 3000), P=4, dtype="mxfp4"), 1, "paged"),
 ]
 
 
 def _ids(x):
-    return getattr(x, "name", str(x))
+    return f"{x.name}-{x.dtype}" if hasattr(x, "name") else str(x)
 
 
 def _newest(t, ctx, n_new):

@@ -44,6 +44,8 @@ CASES = [
     (configs.MXFP4_RAGGED, True, "short_long"),
     (configs.DEEPSEEK_MLA, False, "ends"),
     (configs.DEEPSEEK_MLA, True, "ends"),
+    (configs.DEEPSEEK_MLA_FP8, True, "ends"),
+    (configs.DEEPSEEK_MLA_MXFP4, True, "ends"),
 ]
 
 # MLA groups hold 128 query heads: the oracle checks heads at both ends of
@@ -70,7 +72,8 @@ def test_full_size_sampled_groups(w, needles, sample):
     torch.cuda.empty_cache()
 
 
-STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, configs.DEEPSEEK_MLA]
+STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, configs.DEEPSEEK_MLA,
+              configs.DEEPSEEK_MLA_MXFP4]
 
 
 @pytest.mark.parametrize("w", STEP_CASES, ids=lambda x: x.name)

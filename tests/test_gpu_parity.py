@@ -113,6 +113,8 @@ PLACEMENT_CASES = [
     configs.FP8_GQA.scaled(B=3, Hkv=1, ctx=None, ctx_range=(1, 400), P=4),
     configs.MXFP4_RAGGED.scaled(B=3, Hkv=2, Hq=4, ctx_range=(1, 500), P=8),
     configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 200), P=2),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 200), P=2, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 200), P=3, dtype="mxfp4"),
 ]
 
 
@@ -262,6 +264,12 @@ PARITY_CASES = [
     configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4),                 # MLA, ragged
     configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(1, 40), P=8),                   # MLA, empty slices
     configs.DEEPSEEK_MLA.scaled(B=1, ctx=20011, P=2),                                     # MLA, many splits
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4, dtype="fp8_e4m3"),   # quantised MLA
+    configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(1, 40), P=8, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=1, ctx=20011, P=2, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4, dtype="mxfp4"),
+    configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(1, 40), P=8, dtype="mxfp4"),
+    configs.DEEPSEEK_MLA.scaled(B=1, ctx=20011, P=2, dtype="mxfp4"),
 ]
 
 
@@ -442,6 +450,8 @@ ONE_CALL_CASES = [
     configs.MXFP4_RAGGED.scaled(B=2, ctx_range=(1, 9000)),
     configs.LLAMA405B_SHARE.scaled(B=2, ctx=None, ctx_range=(20000, 60000)),      # many splits per slice
     configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4, dtype="mxfp4"),
 ]
 
 
@@ -483,6 +493,8 @@ EDGE_CASES = [
     configs.MXFP4_RAGGED.scaled(B=65, Hkv=1, Hq=7, ctx_range=(1, 500), P=5),              # MXFP4, G = 7, two launches
     configs.LLAMA405B_SHARE.scaled(B=2, Hkv=2, Hq=32, ctx=None, ctx_range=(3000, 30000)),   # G = 16 with 2 KV heads
     configs.DEEPSEEK_MLA.scaled(B=66, ctx=None, ctx_range=(1, 100), P=1),                 # MLA, P = 1, two launches
+    configs.DEEPSEEK_MLA.scaled(B=66, ctx=None, ctx_range=(1, 100), P=1, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=5, ctx=None, ctx_range=(1, 33), P=64, dtype="mxfp4"),   # quantised MLA, P = 64
 ]
 
 

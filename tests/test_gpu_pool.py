@@ -64,7 +64,7 @@ def _stale(pool, inp, seed):
         api.kv_append_paged(pool, k, v, None, None, pos=[0] * w.B, count=[n] + [0] * (w.B - 1))
     else:
         k = (torch.randn(w.B, w.Hkv, n, w.Dk, generator=g, device=DEV)).to(torch.bfloat16)
-        v = (torch.randn(w.B, w.Hkv, n, w.Dv, generator=g, device=DEV)).to(torch.bfloat16)
+        v = None if w.v_alias_k else (torch.randn(w.B, w.Hkv, n, w.Dv, generator=g, device=DEV)).to(torch.bfloat16)
         api.kv_append_bf16_paged(pool, k, v, pos=[0] * w.B, count=[n] + [0] * (w.B - 1))
     torch.cuda.synchronize()
     pool.release(0)
@@ -98,6 +98,8 @@ CASES = [
     configs.MXFP4_RAGGED.scaled(B=3, Hkv=2, Hq=16, ctx_range=(1, 4000), P=3),
     configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4),
     configs.LLAMA405B_SHARE.scaled(B=1, ctx=40000, P=2),                     # many splits per slice
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=4, dtype="fp8_e4m3"),
+    configs.DEEPSEEK_MLA.scaled(B=2, ctx=None, ctx_range=(1, 3000), P=3, dtype="mxfp4"),
 ]
 
 
