@@ -17,7 +17,7 @@ steps is bracketed by the library's launch trace (HIP events recorded on the
 launch's stream right after it), which gives each kernel's duration.  Prints
 one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-extra]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME] [--no-extra]
 """
 
 import argparse
@@ -440,7 +440,7 @@ def copy_rates(nbytes=4 << 30, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(configs.ALL))
     ap.add_argument("--q-heads", type=int, default=0,
@@ -511,6 +511,12 @@ def main():
                 continue
             extras[name] = measure(configs.ALL[name], args, args.steps, args.warmup, args.append, args.attn,
                                    args.layout, 0 if args.no_cpu_baseline else args.extra_cpu_budget, flags=flags)
+            if name == configs.TINY_GQA.name and not args.flush_cache:
+                # the cache-resident step again with the caches flushed before every step
+                fl = measure(configs.ALL[name], args, args.steps, args.warmup, args.append, args.attn, args.layout, 0,
+                             flags=flags, flush=True)
+                extras[name]["flushed"] = {"step_us": fl["step_us"], "timing_us": fl["timing_us"],
+                                           "kernels_us": fl["kernels_us"]}
     rates = copy_rates()
     log(f"[bench] device copy {rates['copy_gbs']:.0f} GB/s (read + write), plain streaming read "
         f"{rates['read_gbs']:.0f} GB/s; run took {time.time() - t_start:.0f}s")
