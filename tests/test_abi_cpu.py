@@ -377,6 +377,30 @@ def test_quantising_append_argument_checks():
         assert call([0, 0]) == _lib.HX_EHIP               # valid arguments reach the launch
 
 
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "mxfp4"])
+def test_quantised_mla_cache_argument_checks(dtype):
+    """Quantised MLA caches: one packed plane (k), latent rows only (no V
+    input), for the quantising and the storage-format appends and the step."""
+    L = _lib.lib()
+    d = api.KVDesc(P=4, B=2, Hkv=1, Dk=576, Dv=512, v_alias_k=True, dtype=dtype, cap=64)
+    one = _lib.hx_kv_cache(0x50000, None, None, None)
+    pa = (ctypes.c_int64 * 2)(0, 0)
+
+    def bf16(k=0x10000, v=None, c=one):
+        return L.hx_kv_append_bf16(ctypes.byref(d.c()), ctypes.byref(c), _fake(k), _fake(v), pa, None, 4, None)
+
+    assert bf16(v=0x20000) == _lib.HX_EINVAL                               # V aliases K: no v_new
+    assert bf16(k=0) == _lib.HX_EINVAL
+    assert bf16(c=_lib.hx_kv_cache(0x50000, None, 0x70000, None)) == _lib.HX_EINVAL   # packed: one plane
+    assert bf16(c=_lib.hx_kv_cache(0x50000, 0x60000, None, None)) == _lib.HX_EINVAL
+    assert L.hx_kv_append(ctypes.byref(d.c()), ctypes.byref(one), _fake(0x10000), _fake(0x20000), _fake(0x30000),
+                          None, pa, None, 4, None) == _lib.HX_EINVAL        # storage format: no v_new either
+    assert L.hx_kv_append(ctypes.byref(d.c()), ctypes.byref(one), _fake(0x10000), None, None, None, pa, None, 4,
+                          None) == _lib.HX_EINVAL                           # scales are required
+    if not torch.cuda.is_available():
+        assert bf16() == _lib.HX_EHIP                                      # valid arguments reach the launch
+
+
 def test_dequant_and_combine_argument_checks():
     L = _lib.lib()
     d = DESCS[0]
