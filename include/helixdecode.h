@@ -295,8 +295,10 @@ hx_status hx_decode_attn_noalloc(const hx_kv_desc* desc, const hx_kv_cache* cach
  * writes the row before it reads the tile (one launch fewer than append +
  * attention; the cache afterwards holds exactly what hx_kv_append writes).
  * MXFP4 caches take the append kernel first instead (their fused kernel was
- * slower than the launch it saves).  Helix summary, paragraphs on Helix's
- * two layouts (new KV written round-robin as produced) and on KV
+ * slower than the launch it saves), and so do quantised MLA caches (their
+ * kernel converts tiles in LDS before reading them); all arguments are
+ * checked before the cache is written.  Helix summary, paragraphs on
+ * Helix's two layouts (new KV written round-robin as produced) and on KV
  * parallelism. */
 hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const void* k_new, const void* v_new,
                          const void* k_scale_new, const void* v_scale_new, int32_t n_new, const void* q, int32_t Hq,
@@ -313,6 +315,8 @@ hx_status hx_decode_step(const hx_kv_desc* desc, const hx_kv_cache* cache, const
  * format: the partial kernel (which quantises first), then the fold into O
  * and LSE.  The cache afterwards holds exactly what hx_kv_append_bf16
  * writes, and O / LSE equal hx_kv_append_bf16 followed by hx_decode_attn.
+ * Quantised MLA caches take the quantising append kernel first (three
+ * launches; all arguments are checked before the cache is written).
  * A bf16 cache takes the rows as storage format (= hx_decode_step).  Other
  * arguments, checks and errors as hx_decode_step.  Helix summary,
  * paragraphs on Helix's two layouts (new KV written round-robin as
