@@ -1,166 +1,18 @@
-// The append of new rows into chunk tiles, as a device function shared by
-// the append kernel and the fused decode step (the partial kernels append a
-// step's rows into the tiles they own before streaming them).
+// The append of a decode step's new rows into the chunk tiles it owns, as
+// device functions the partial kernels run before streaming those tiles
+// (hx_decode_step, hx_decode_step_bf16): the storage-format copy through
+// the forward tile map (append_rows) and the quantising form (fused_quant,
+// with quant_tile of hx_quant.h, the append kernel's own encoder).  The
+// standalone append kernel (kv_cache.hip) owns destination bytes instead.
 //
 // Placement (Helix summary, paragraph on Helix's two layouts; NVIDIA blog,
 // section on distributed KV placement): token t of a request belongs to the
 // 16-token group c = t / 16, which lives in slice c mod P as that slice's
-// (c / P)-th chunk tile.  One call owns destination bytes, not source
-// tokens: a 16-byte piece of one chunk tile of one plane, built from the new
-// rows that fall in it and the stored bytes of the others.  No two pieces
-// share bytes, so concurrent calls on different pieces do not depend on
-// their order, and bytes move unconverted (bit-exact).
+// (c / P)-th chunk tile.
 #pragma once
 
 #include "hx_common.h"
 #include "hx_quant.h"
-
-namespace hx {
-
-// 16-byte pieces of all planes of one chunk tile (a fp8 group scale counts
-// as one piece).
-__device__ __forceinline__ int64_t append_pieces(const AppendArgs& a, int64_t* pieces) {
-  int64_t sum = 0;
-  for (int p = 0; p < a.nplanes; ++p) {
-    pieces[p] = a.ebits[p] == 32 ? 1 : (a.tile_bytes[p] + 15) / 16;
-    sum += pieces[p];
-  }
-  return sum;
-}
-
-// Piece `piece` (over all planes, in plane order) of the chunk tile holding
-// request-level group pos / 16 + ci of request bl of the launch, KV head g.
-__device__ __forceinline__ void append_piece(const AppendArgs& a, int bl, int g, int ci, int64_t piece) {
-  int64_t pieces[4];
-  append_pieces(a, pieces);
-  int plane = 0;
-  while (piece >= pieces[plane]) piece -= pieces[plane++];
-
-  const int b = a.b0 + bl;
-  const int64_t pos = a.pos[bl];
-  const int64_t end = pos + a.count[bl];
-  const int64_t c = pos / kChunk + ci;           // request-level chunk (group) index
-  const int64_t row0 = c * kChunk;
-  if (end == pos || row0 >= end) return;   // nothing of this request lands in this chunk
-  int r;
-  int64_t lc;
-  if (c <= 0xffffffffll) {
-    r = (int)((uint32_t)c % (uint32_t)a.P);
-    lc = (uint32_t)c / (uint32_t)a.P;
-  } else {
-    r = (int)(c % a.P);
-    lc = c / a.P;
-  }
-  const int64_t tile = tile_of(TileMap{a.table, a.num_blocks, a.P, a.B, a.Hkv, a.cap_chunks}, r, b, g, lc);
-  const int64_t src_tok0 = ((int64_t)bl * a.Hkv + g) * a.n_new;   // token-major source, this launch's rows
-  const uint8_t* src = a.src[plane];
-  uint8_t* dst = a.dst[plane] + tile * a.tile_stride[plane];
-
-  if (a.ebits[plane] == 32) {
-    // one fp32 scale per chunk: a chunk whose first row is new takes the scale
-    // of that row; a chunk that already holds rows keeps its stored scale
-    if (row0 < pos) return;
-    const float v = reinterpret_cast<const float*>(src)[src_tok0 + (row0 - pos)];
-    *reinterpret_cast<float*>(dst) = v;
-    return;
-  }
-
-  const int64_t byte0 = piece * 16;
-  const int nbytes = (int)((a.tile_bytes[plane] - byte0) < 16 ? (a.tile_bytes[plane] - byte0) : 16);
-  const int eb = a.ebits[plane];
-  const int lay = a.lay[plane], width = a.width[plane];
-  const int64_t srow = a.src_row_bytes[plane];
-  const int nelem = eb == 16 ? nbytes / 2 : (eb == 8 ? nbytes : 2 * nbytes);
-  auto elem_off2 = [&](int e) -> int64_t {
-    return eb == 16 ? 2 * (byte0 + 2 * e) : (eb == 8 ? 2 * (byte0 + e) : 2 * byte0 + e);
-  };
-  // a piece holding none of the new rows stays as it is: first a cheap test
-  // on the piece's row range, then the exact one
-  {
-    int mlo, mhi;
-    piece_rows(lay, width, byte0, nbytes, &mlo, &mhi);
-    if (row0 + mhi < pos || row0 + mlo >= end) return;
-  }
-  bool any = false;
-  for (int e = 0; e < nelem; ++e) {
-    int mm, d;
-    tile_inv(lay, width, elem_off2(e), &mm, &d);
-    any |= row0 + mm >= pos && row0 + mm < end;
-  }
-  if (!any) return;
-  const bool whole = row0 >= pos && row0 + kChunk <= end;
-  if (!whole && nbytes == 16 && eb != 4) {
-    // part of the piece is new (a decode step's row): store just the new 1- or
-    // 2-byte elements, so the stored bytes of other rows are not read; every
-    // source element is loaded before the first store (the source and the
-    // planes might alias as far as the compiler knows, so interleaved loads
-    // and stores would serialise on memory latency)
-    if (eb == 16) {
-      uint16_t v[8];
-      bool nw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int mm, d;
-        tile_inv(lay, width, elem_off2(e), &mm, &d);
-        const int64_t tok = row0 + mm;
-        nw[e] = tok >= pos && tok < end;
-        v[e] = nw[e] ? *reinterpret_cast<const uint16_t*>(src + (src_tok0 + (tok - pos)) * srow + 2 * d) : 0;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (nw[e]) *reinterpret_cast<uint16_t*>(dst + byte0 + 2 * e) = v[e];
-    } else {
-      uint8_t v[16];
-      bool nw[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int mm, d;
-        tile_inv(lay, width, elem_off2(e), &mm, &d);
-        const int64_t tok = row0 + mm;
-        nw[e] = tok >= pos && tok < end;
-        v[e] = nw[e] ? src[(src_tok0 + (tok - pos)) * srow + d] : 0;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (nw[e]) dst[byte0 + e] = v[e];
-    }
-    return;
-  }
-  uint8_t buf[16];
-  if (nbytes == 16) {
-    const uint4 v = whole ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(dst + byte0);
-    __builtin_memcpy(buf, &v, 16);
-  } else {
-    for (int i = 0; i < nbytes; ++i) buf[i] = dst[byte0 + i];
-  }
-  for (int e = 0; e < nelem; ++e) {
-    int mm, d;
-    tile_inv(lay, width, elem_off2(e), &mm, &d);
-    const int64_t tok = row0 + mm;
-    if (tok < pos || tok >= end) continue;
-    const uint8_t* srcrow = src + (src_tok0 + (tok - pos)) * srow;
-    if (eb == 16) {
-      buf[2 * e] = srcrow[2 * d];
-      buf[2 * e + 1] = srcrow[2 * d + 1];
-    } else if (eb == 8) {
-      buf[e] = srcrow[d];
-    } else {   // 4-bit codes, even element in the low nibble of the source
-      const uint8_t sb = srcrow[d >> 1];
-      const uint8_t code = (d & 1) ? (sb >> 4) : (sb & 0xf);
-      uint8_t& o = buf[e >> 1];
-      o = (e & 1) ? (uint8_t)((o & 0x0f) | (code << 4)) : (uint8_t)((o & 0xf0) | code);
-    }
-  }
-  if (nbytes == 16) {
-    uint4 v;
-    __builtin_memcpy(&v, buf, 16);
-    *reinterpret_cast<uint4*>(dst + byte0) = v;
-  } else {
-    for (int i = 0; i < nbytes; ++i) dst[byte0 + i] = buf[i];
-  }
-}
-
-}  // namespace hx
 
 namespace hx {
 
