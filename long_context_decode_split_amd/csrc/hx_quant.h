@@ -104,13 +104,21 @@ __device__ __forceinline__ float block_max(float v, float* s_red, int tid, int n
 constexpr int kQuantMaxBlocks = 576 / 32;
 
 // Quantises the new rows of one tile (fp8: one K or V tile and its scale;
-// MXFP4: one K or V code tile and its row exponents).  Called by all nthr
+// MXFP4: one K or V code tile and its row exponents; quant_tile below picks
+// the layout's instantiation).  Called by all nthr
 // threads of a workgroup (nthr a multiple of 64, at most 1024), uniformly;
 // s_red: nthr / 64 floats of LDS, s_e: 16 x kQuantMaxBlocks bytes of LDS.
-__device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr, float* s_red, uint8_t* s_e) {
+// LAY is the tile layout as a compile-time constant, so the layout switches
+// of the element maps fold away (quant_tile below dispatches on j.lay).
+template <int LAY>
+__device__ __forceinline__ void quant_tile_lay(const QuantJob& j, int tid, int nthr, float* s_red, uint8_t* s_e) {
   using namespace quant;
-  const int D = j.D, lay = j.lay;
-  if (j.dtype == HX_KV_FP8_E4M3) {
+  const int D = j.D;
+  constexpr int lay = LAY;
+  // the layout fixes the format: fp8 codes (GQA tiles, MLA row-major bytes)
+  // or MXFP4 codes (GQA tiles, MLA row-major nibbles)
+  constexpr bool kFp8 = LAY == kLayGqaFp8K || LAY == kLayGqaFp8V || LAY == kLayRowU8;
+  if constexpr (kFp8) {
     float* scp = reinterpret_cast<float*>(j.sc);
     // amax of the new rows, and whether a stored code of the group is non-zero
     float amax = 0.f, nz = 0.f;
@@ -187,6 +195,17 @@ __device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr,
       if (touched) *reinterpret_cast<uint32_t*>(j.tile + byte0) = w;
     }
     __syncthreads();   // s_e is free again
+  }
+}
+
+__device__ __forceinline__ void quant_tile(const QuantJob& j, int tid, int nthr, float* s_red, uint8_t* s_e) {
+  switch (j.lay) {   // uniform over the workgroup
+    case kLayGqaFp8K: quant_tile_lay<kLayGqaFp8K>(j, tid, nthr, s_red, s_e); break;
+    case kLayGqaFp8V: quant_tile_lay<kLayGqaFp8V>(j, tid, nthr, s_red, s_e); break;
+    case kLayGqaFp4K: quant_tile_lay<kLayGqaFp4K>(j, tid, nthr, s_red, s_e); break;
+    case kLayGqaFp4V: quant_tile_lay<kLayGqaFp4V>(j, tid, nthr, s_red, s_e); break;
+    case kLayRowU4: quant_tile_lay<kLayRowU4>(j, tid, nthr, s_red, s_e); break;
+    default: quant_tile_lay<kLayRowU8>(j, tid, nthr, s_red, s_e); break;
   }
 }
 
