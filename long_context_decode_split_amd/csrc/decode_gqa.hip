@@ -194,7 +194,7 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
   }
 
   // ---- online softmax (base 2)
-  float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  float cm = fmaxf(vmax(sc[0], sc[1]), vmax(sc[2], sc[3]));
   cm = max_xor32(max_xor16(cm));
   // The reference max mrun moves only when some head's scores exceed it by
   // more than kHeadroom: P = 2^(s - mrun) is bounded by 2^kHeadroom, and the

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
       }
       // ---- online softmax (base 2): the reference moves only when some
       //      head's scores exceed it by more than the headroom
-      float cm = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])), fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+      float cm = fmaxf(fmaxf(vmax(s8[0], s8[1]), vmax(s8[2], s8[3])), fmaxf(vmax(s8[4], s8[5]), vmax(s8[6], s8[7])));
       cm = max_xor32(max_xor16(cm));
       const float cms = FMT == 1 ? cm : cm * c2;
       if (__any(cms > mrun[i] + kHeadroomW<FMT>)) {   // wave-uniform

@@ -82,13 +82,27 @@ __device__ __forceinline__ uint2 swap_rows32(float x) {
   return make_uint2(__float_as_uint(x), __float_as_uint(x));   // host pass: never called
 #endif
 }
+// max(a, b) as one v_med3_f32(a, b, +inf).  fmaxf under the IEEE mode that
+// kernels run in makes the compiler quiet every operand it cannot prove
+// canonical (matrix-core results, lane permutes) with an extra v_max_f32
+// x, x first; the median against +inf needs none.  The +inf is opaque to
+// the optimiser, which would otherwise fold the median back into fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float inf = INFINITY;
+  asm("" : "+v"(inf));
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+#else
+  return a > b ? a : b;   // host pass: never called
+#endif
+}
 __device__ __forceinline__ float max_xor16(float x) {
   const uint2 s = swap_rows16(x);
-  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+  return vmax(__uint_as_float(s.x), __uint_as_float(s.y));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const uint2 s = swap_rows32(x);
-  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+  return vmax(__uint_as_float(s.x), __uint_as_float(s.y));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   const uint2 s = swap_rows16(x);
