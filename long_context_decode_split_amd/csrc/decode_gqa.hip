@@ -308,10 +308,9 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
 
   // ---- which (request, KV head, slice, split) this workgroup owns
   const int wg = blockIdx.x;
-  int bl = 0;
-  while (bl + 1 < a.nb && a.wg_begin[bl + 1] <= wg) ++bl;
+  int rem;
+  const int bl = request_of(a, wg, &rem);
   const int nsplit = a.nsplit[bl];
-  int rem = wg - a.wg_begin[bl];
   const int split = rem % nsplit;
   rem /= nsplit;
   const int r = rem % a.P;
@@ -320,8 +319,8 @@ __global__ __launch_bounds__(64 * WAVES) void gqa_partial_kernel(const PartialAr
 
   const int64_t L = slice_len(a.n[bl], a.P, r);
   const int nch = (int)((L + kChunk - 1) / kChunk);
-  const int c0 = split * a.cpw;
-  const int c1 = min(c0 + a.cpw, nch);
+  const int c0 = split * a.cpw_b[bl];
+  const int c1 = min(c0 + a.cpw_b[bl], nch);
   // the step's new rows of these tiles first: copied (storage format) or quantised from bf16
   if constexpr (FUSE == 1) fused_append(a.app, bl, g, r, c0, c1);
   if constexpr (FUSE == 2) fused_quant(a.app, bl, g, r, c0, c1);

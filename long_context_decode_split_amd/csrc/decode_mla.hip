@@ -195,10 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
 
   // ---- which (request, latent head, slice, split) this workgroup owns
   const int wg = blockIdx.x;
-  int bl = 0;
-  while (bl + 1 < a.nb && a.wg_begin[bl + 1] <= wg) ++bl;
+  int rem;
+  const int bl = request_of(a, wg, &rem);
   const int nsplit = a.nsplit[bl];
-  int rem = wg - a.wg_begin[bl];
   const int split = rem % nsplit;
   rem /= nsplit;
   const int r = rem % a.P;
@@ -206,8 +205,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   const int b = a.b0 + bl;
 
   const int64_t L = slice_len(a.n[bl], a.P, r);
-  const int64_t t_begin = (int64_t)split * a.cpw * kChunk;   // cpw is even: tiles start on 32 rows
-  const int64_t t_end = min((int64_t)(split + 1) * a.cpw * kChunk, L);
+  const int64_t t_begin = (int64_t)split * a.cpw_b[bl] * kChunk;   // cpw_b is even: tiles start on 32 rows
+  const int64_t t_end = min((int64_t)(split + 1) * a.cpw_b[bl] * kChunk, L);
   const int ntok = t_end > t_begin ? (int)(t_end - t_begin) : 0;
   const int ntiles = (ntok + kTileTok - 1) / kTileTok;
 

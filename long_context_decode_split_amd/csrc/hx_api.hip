@@ -228,6 +228,19 @@ int target_wgs(int kind, int dtype, int G) {
   return std::min(bound, device_cus() * per_cu);
 }
 
+// Workgroups per launch for a batch whose one-round plan above overflows its
+// round (ragged contexts: each slice's last split is short, so the slices
+// need more splits in all than the target): narrow bf16 and fp8 groups then
+// take eight workgroups per CU, several rounds whose shorter workgroups
+// (dispatched last) fill the end of the launch.  Measured on 16 requests of
+// 4K-2M tokens: bf16 1,492 -> 1,438 us, fp8 768 -> 741 us (four per CU); on
+// uniform contexts one round stays best (1M tokens: 652 us at two per CU,
+// 657 at four).  0: no such re-plan (other kernels, or HX_WGS_PER_CU set).
+int overflow_target_wgs(int kind, int dtype, int G) {
+  if (kind != 0 || G > kGqaNarrowMaxHeads || dtype == HX_KV_MXFP4 || getenv("HX_WGS_PER_CU")) return 0;
+  return std::min(kGqaTargetWgs, device_cus() * 8);
+}
+
 // Smallest split (chunk tiles per workgroup): GQA waves each take one tile in
 // turn, so four per wave keep their loads pipelined; MLA tiles come in pairs.
 // HX_MIN_CHUNKS_PER_WG overrides (tuning knob).
@@ -693,8 +706,11 @@ static int plan_launch(const hx_kv_desc& d, const Geometry& geo, const int64_t* 
   }
   int64_t nch_max = 1;
   for (int i = 0; i < nb; ++i) nch_max = std::max(nch_max, nch[i]);
-  int64_t cpw = std::max<int64_t>(minc, (W + target - 1) / target);
-  cpw = std::max<int64_t>(cpw, (nch_max + kMaxSplits - 1) / kMaxSplits);
+  auto split_size = [&](int tgt) {
+    const int64_t c = std::max<int64_t>(minc, (W + tgt - 1) / tgt);
+    return std::max<int64_t>(c, (nch_max + kMaxSplits - 1) / kMaxSplits);
+  };
+  int64_t cpw = split_size(target);
   // short contexts: slices of at most kShortSliceChunks tiles are not split
   // (one workgroup per slice, no fold launch; measured faster on the
   // 4,096-token single-request step, where fixed launch costs dominate).
@@ -704,18 +720,47 @@ static int plan_launch(const hx_kv_desc& d, const Geometry& geo, const int64_t* 
   const bool short_mode = nch_max <= kShortSliceChunks && (!final_out || env_int("HX_SHORT_ONE_CALL", 0, 0, 1));
   if (short_mode) cpw = std::max<int64_t>(cpw, nch_max);
   a.waves = geo.kind == 0 && short_mode ? kGqaShortWaves : kGqaWavesPerWg;
-  if (geo.kind == 1 || G > kGqaNarrowMaxHeads) cpw += cpw & 1;   // MLA and wide-GQA tiles come in pairs
-  a.cpw = (int)std::min<int64_t>(cpw, 1 << 30);
-  int wgs = 0, folds = 0;
+  const bool pairs = geo.kind == 1 || G > kGqaNarrowMaxHeads;   // MLA and wide-GQA tiles come in pairs
+  // splits of every request for split size cpw: as even as its split count
+  // allows (the last split of a slice is otherwise the remainder, up to
+  // cpw - 1 tiles short), pairs kept whole; returns the workgroup count
+  auto splits = [&](int64_t c) {
+    if (pairs) c += c & 1;
+    a.cpw = (int)std::min<int64_t>(c, 1 << 30);
+    int64_t total = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int64_t ns = (nch[i] + a.cpw - 1) / a.cpw;
+      int64_t cb = (nch[i] + ns - 1) / ns;
+      if (pairs) cb += cb & 1;
+      a.cpw_b[i] = (int)cb;
+      a.nsplit[i] = (int)((nch[i] + cb - 1) / cb);
+      total += (int64_t)a.nsplit[i] * d.Hkv * d.P;
+    }
+    return total;
+  };
+  const int64_t total = splits(cpw);
+  const int over = short_mode ? 0 : overflow_target_wgs(geo.kind, d.dtype, G);
+  if (over > 0 && total > target) splits(split_size(over));
+  int folds = 0;
   for (int i = 0; i < nb; ++i) {
-    a.nsplit[i] = (int)((nch[i] + a.cpw - 1) / a.cpw);
-    a.wg_begin[i] = wgs;
     a.fold_begin[i] = folds;
-    wgs += a.nsplit[i] * d.Hkv * d.P;
     if (a.nsplit[i] > 1) folds += d.Hkv * d.P * G;
   }
-  a.wg_begin[nb] = wgs;
   a.fold_begin[nb] = folds;
+  // Workgroups of the requests with the longest splits first: the hardware
+  // starts workgroups in index order as slots free up, so the shorter ones
+  // fill the end of the launch.
+  for (int i = 0; i < nb; ++i) a.order[i] = i;
+  std::stable_sort(a.order, a.order + nb, [&](int x, int y) { return a.cpw_b[x] > a.cpw_b[y]; });
+  int wgs = 0;
+  for (int p = 0; p < nb; ++p) {
+    const int i = a.order[p];
+    a.pos_begin[p] = wgs;
+    a.wg_begin[i] = wgs;
+    wgs += a.nsplit[i] * d.Hkv * d.P;
+  }
+  a.pos_begin[nb] = wgs;
+  a.wg_begin[nb] = wgs;
   return wgs;
 }
 

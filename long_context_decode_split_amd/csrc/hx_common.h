@@ -347,14 +347,29 @@ struct PartialArgs {
   int fused_append;        // the workgroups first append app's rows into the tiles they own:
                            // 0 no, 1 storage-format rows, 2 bf16 rows quantised (app.quant)
   AppendArgs app;          // (same requests as this launch: app.b0 = b0)
-  int cpw;                 // chunks per workgroup (split size)
+  int cpw;                 // chunks per workgroup (split size), the largest over the requests
   int waves;               // GQA: waves per workgroup (kGqaWavesPerWg, or kGqaShortWaves for unsplit slices)
   int64_t n[kMaxBatchPerLaunch];
   int nsplit[kMaxBatchPerLaunch];
-  int wg_begin[kMaxBatchPerLaunch + 1];     // first workgroup (= split record) of each request
+  int cpw_b[kMaxBatchPerLaunch];            // split size of each request: its slices' tiles spread evenly
+  int wg_begin[kMaxBatchPerLaunch + 1];     // first workgroup (= split record) of each request; [nb]: the total
   int fold_begin[kMaxBatchPerLaunch + 1];   // first fold workgroup of each request
+  // dispatch order: the requests' workgroup ranges follow one another in the
+  // order order[0], order[1], ... (longest splits first), the range of
+  // order[i] starting at workgroup pos_begin[i] (= wg_begin[order[i]])
+  int order[kMaxBatchPerLaunch];
+  int pos_begin[kMaxBatchPerLaunch + 1];
 };
 HXHD TileMap tile_map(const PartialArgs& a) { return TileMap{a.table, a.num_blocks, a.P, a.Btot, a.Hkv, a.cap_chunks}; }
+
+// The request (index in the launch) that workgroup wg belongs to, and wg's
+// index among that request's workgroups.
+__device__ __forceinline__ int request_of(const PartialArgs& a, int wg, int* rem) {
+  int i = 0;
+  while (i + 1 < a.nb && a.pos_begin[i + 1] <= wg) ++i;
+  *rem = wg - a.pos_begin[i];
+  return a.order[i];
+}
 
 hipError_t launch_gqa_partial(const PartialArgs& a, int dtype, hipStream_t st);
 // GQA groups of more than 16 query heads (decode_gqa_wide.hip): tiles in

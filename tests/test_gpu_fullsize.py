@@ -35,6 +35,9 @@ def _step(inp):
     return o_part, lse_part, o, lse
 
 
+RAGGED_BF16 = configs.MXFP4_RAGGED.scaled(name="ragged_bf16", dtype="bf16")
+RAGGED_FP8 = configs.MXFP4_RAGGED.scaled(name="ragged_fp8", dtype="fp8_e4m3")
+
 CASES = [
     (configs.LLAMA405B_SHARE, False, "ends"),
     (configs.LLAMA405B_SHARE, True, "ends"),
@@ -42,6 +45,12 @@ CASES = [
     (configs.FP8_GQA, True, "ends"),
     (configs.MXFP4_RAGGED, False, "short_long"),
     (configs.MXFP4_RAGGED, True, "short_long"),
+    # the ragged batch in bf16 and fp8: its one-round split plan needs more
+    # workgroups than one round holds (each slice's last split is short), so
+    # the launch is planned again with more, shorter workgroups, dispatched
+    # longest first
+    (RAGGED_BF16, False, "short_long"),
+    (RAGGED_FP8, True, "short_long"),
     (configs.DEEPSEEK_MLA, False, "ends"),
     (configs.DEEPSEEK_MLA, True, "ends"),
     (configs.DEEPSEEK_MLA_FP8, True, "ends"),
@@ -72,7 +81,7 @@ def test_full_size_sampled_groups(w, needles, sample):
     torch.cuda.empty_cache()
 
 
-STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, configs.DEEPSEEK_MLA,
+STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, RAGGED_BF16, configs.DEEPSEEK_MLA,
               configs.DEEPSEEK_MLA_MXFP4]
 
 
@@ -100,7 +109,7 @@ def test_full_size_fused_step(w):
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)) and torch.equal(l1.view(torch.int32), l2.view(torch.int32))
     oc, lc = o2.cpu().numpy(), l2.cpu().numpy()
     del cache, ws
-    if w.name == configs.MXFP4_RAGGED.name:
+    if w.ctx is None:   # ragged: the shortest and the longest request
         groups = [(min(range(w.B), key=lambda b: inp.ctx[b]), 0), (max(range(w.B), key=lambda b: inp.ctx[b]), 0)]
     else:
         groups = [(0, 0), (w.B - 1, w.Hkv - 1)]
