@@ -217,8 +217,8 @@ int target_wgs(int kind, int dtype, int G) {
   // resident); MXFP4 splits are short in time (a quarter of the bf16 bytes
   // per row) and three workgroups fit per CU, so eight per CU keep the
   // rounds even (measured: 475 us at four, 445 us at eight on the ragged
-  // 16-request cache).  The MLA kernel holds 152 KiB of LDS: one workgroup
-  // of eight waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
+  // 16-request cache).  The MLA kernel holds 144 KiB of LDS: one workgroup
+  // of four waves per CU.  HX_WGS_PER_CU overrides (tuning knob).
   // Wide GQA groups (LDS-shared tile pairs, decode_gqa_wide.hip) run best
   // with four workgroups per CU for bf16 and eight for fp8 and MXFP4 pairs.
   const bool wide = kind == 0 && G > kGqaNarrowMaxHeads;
