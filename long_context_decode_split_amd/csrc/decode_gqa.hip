@@ -30,6 +30,8 @@
 // per workgroup (8 for short unsplit slices), and whether the workgroup first
 // appends a decode step's new rows into its tiles (hx_decode_step).
 
+#include <type_traits>
+
 #include "hx_append.h"
 #include "hx_gqa_frag.h"
 
@@ -261,24 +263,27 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
     }
   } else {
     // Per (token, 32-column block) scales are powers of two: fold them into
-    // P, one P fragment per block.  Scaling by a power of two commutes with
-    // the rounding to bf16 (outside the subnormal range), so the sum of the
-    // rounded, unscaled P is what normalises O.
-    const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+    // P, one P fragment per block, by adding them into the exponents of P's
+    // bf16 pairs (scale_bf16x2_e8m0), which gives the rounded product.  So
+    // the sum of the rounded, unscaled P is what normalises O.  P enters
+    // clamped at 2^-126 below (a weight that small relative to the reference
+    // adds at most 2^-126 |V| per row; an exact 0 would not stay 0 through
+    // the exponent arithmetic).
+    const float kMinP = 1.17549435e-38f;   // 2^-126
+    const uint32_t p01 = pack_bf16(fmaxf(p[0], kMinP), fmaxf(p[1], kMinP));
+    const uint32_t p23 = pack_bf16(fmaxf(p[2], kMinP), fmaxf(p[3], kMinP));
     st.lsum_mfma = add_bf16x2(p23, add_bf16x2(p01, st.lsum_mfma));
     const uint32_t vs[4] = {cur.vsc.x, cur.vsc.y, cur.vsc.z, cur.vsc.w};   // token 4h+j: 4 block scales
     const uint32_t w[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      float ps[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ps[j] = p[j] * e8m0_sel(vs[j], blk);
+    auto block = [&](auto blk_t) {
+      constexpr int blk = decltype(blk_t)::value;
+      uint32_t s01 = scale_bf16x2_e8m0(p01, e8m0_pair<blk>(vs[0], vs[1]));
+      uint32_t s23 = scale_bf16x2_e8m0(p23, e8m0_pair<blk>(vs[2], vs[3]));
       if constexpr (TAIL) {   // rows past the slice end may hold any scale byte
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * h + j >= valid) ps[j] = 0.f;
+        s01 &= keep01;
+        s23 &= keep23;
       }
-      const s16x4 pb = as_s16x4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]));
+      const s16x4 pb = as_s16x4(s01, s23);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const int nb = 2 * blk + hb;   // bytes 2nb, 2nb+1 of the lane's 16 B
@@ -293,7 +298,11 @@ __device__ __forceinline__ void chunk_step(const Frag<FMT>& cur, WaveState& st, 
         }
         st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(lo & keep01, hi & keep23), pb, st.acc[nb], 0, 0, 0);
       }
-    }
+    };
+    block(std::integral_constant<int, 0>{});
+    block(std::integral_constant<int, 1>{});
+    block(std::integral_constant<int, 2>{});
+    block(std::integral_constant<int, 3>{});
   }
 }
 

@@ -137,7 +137,7 @@ __device__ __forceinline__ void wait_pairs(int q) {
 }
 
 template <int FMT, bool PAGED, int W, int NHW, int FUSE>
-__global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
+__global__ __launch_bounds__(64 * W, NHW > 1 ? 2 : 1) void gqa_wide_kernel(const PartialArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (LDS address space) below
   using Lay = PairLay<FMT>;
   constexpr int kNBuf = kRing<FMT>;
@@ -454,28 +454,38 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
           acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, PB, acc[i][nb], 0, 0, 0);
         }
       } else {
-        // per (token, 32-column block) power-of-two scales folded into P, one
-        // P fragment per block; the sum of the rounded, unscaled P
-        // normalises O (a power-of-two scaling commutes with the rounding)
+        // per (token, 32-column block) power-of-two scales added into the
+        // exponents of P's bf16 pairs (scale_bf16x2_e8m0: the rounded
+        // product), one P fragment per block; the sum of the rounded,
+        // unscaled P normalises O.  P is clamped at 2^-126 below (an exact
+        // 0 would not stay 0 through the exponent arithmetic).
+        const float kMinP = 1.17549435e-38f;   // 2^-126
+        uint32_t p2[2][2];   // [tile][tokens 4h+0,1 | 4h+2,3]
         {
           float sm = lsm[i];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) sm = add_bf16x2(pack_bf16(p[2 * q], p[2 * q + 1]), sm);
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              p2[t][q] = pack_bf16(fmaxf(p[4 * t + 2 * q], kMinP), fmaxf(p[4 * t + 2 * q + 1], kMinP));
+              sm = add_bf16x2(p2[t][q], sm);
+            }
           lsm[i] = sm;
         }
         const uint32_t vw[2][4] = {{vsc[0].x, vsc[0].y, vsc[0].z, vsc[0].w}, {vsc[1].x, vsc[1].y, vsc[1].z, vsc[1].w}};
+        auto block = [&](auto blk_t) {
+          constexpr int blk = decltype(blk_t)::value;
+          uint32_t sp[2][2];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          float ps[8];
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float v = p[4 * t + j] * e8m0_sel(vw[t][j], blk);
-              ps[4 * t + j] = FULL || 4 * h + j < (t ? v1 : v0) ? v : 0.f;   // rows past the slice: any scale byte
+          for (int t = 0; t < 2; ++t) {
+            sp[t][0] = scale_bf16x2_e8m0(p2[t][0], e8m0_pair<blk>(vw[t][0], vw[t][1]));
+            sp[t][1] = scale_bf16x2_e8m0(p2[t][1], e8m0_pair<blk>(vw[t][2], vw[t][3]));
+            if constexpr (!FULL) {   // rows past the slice: any scale byte
+              sp[t][0] &= keep01[t];
+              sp[t][1] &= keep23[t];
             }
-          const bf16x8 PB = as_bf16x8(make_uint4(pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3]),
-                                                 pack_bf16(ps[4], ps[5]), pack_bf16(ps[6], ps[7])));
+          }
+          const bf16x8 PB = as_bf16x8(make_uint4(sp[0][0], sp[0][1], sp[1][0], sp[1][1]));
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             const int nb = 2 * blk + hb;   // bytes 2nb, 2nb+1 of the lane's 16 B
@@ -495,7 +505,11 @@ __global__ __launch_bounds__(64 * W) void gqa_wide_kernel(const PartialArgs a) {
             const bf16x8 va = as_bf16x8(make_uint4(lo[0], hi[0], lo[1], hi[1]));
             acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, PB, acc[i][nb], 0, 0, 0);
           }
-        }
+        };
+        block(std::integral_constant<int, 0>{});
+        block(std::integral_constant<int, 1>{});
+        block(std::integral_constant<int, 2>{});
+        block(std::integral_constant<int, 3>{});
       }
     }
   };

@@ -75,6 +75,30 @@ __device__ __forceinline__ float e8m0_sel(uint32_t w, int j) {
   }
 }
 
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+// Bytes J of two e8m0 words a (low half) and b (high half) as the two 16-bit
+// halves of one word: one byte permute.
+template <int J>
+__device__ __forceinline__ uint32_t e8m0_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, (uint32_t)J | 0x0C00u | ((uint32_t)(4 + J) << 16) | 0x0C000000u);
+}
+
+// A bf16 pair p (both halves in [2^-126, 2^9)) times 2^(E_lo - 127) and
+// 2^(E_hi - 127) for the e8m0 pair e (e8m0_pair): E is added into each
+// half's exponent field (bits 7-14; the sum stays below 2^16, so nothing
+// carries into the other half), then 127 is taken off with unsigned
+// saturation.  Exactly the product, a product by a power of two, while it is
+// a normal bf16; below that range it becomes 0 (or, at exponent 0, P's
+// mantissa bits: within 2^-126 of the product).  Products of 2^128 and more
+// (scales above 2^119) are not finite, as in the fp32 product.  Three
+// instructions for two weights, against two shifts, two multiplies and a
+// pack.
+__device__ __forceinline__ uint32_t scale_bf16x2_e8m0(uint32_t p, uint32_t e) {
+  const u16x2 s = __builtin_bit_cast(u16x2, (e << 7) + p);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(s, (u16x2){0x3F80, 0x3F80}));
+}
+
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // c + (sum of a packed bf16 pair), in fp32.
