@@ -250,6 +250,35 @@ def test_fp8_zero_scales_in_the_last_tile():
     H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
 
 
+@pytest.mark.parametrize("hq", [16, 64, 128], ids=["G16", "G64", "G128"])
+def test_mxfp4_value_scales_over_a_wide_exponent_range(hq):
+    """The V block scales of an MXFP4 cache enter the value product through
+    the exponent fields of the bf16 weights (an integer add, no multiply):
+    with the block exponents spread over 2^-60 .. 2^30 of the quantiser's,
+    every output row must stay within the format's relative bound of the
+    oracle's (O then spans many orders of magnitude, so the bound is taken
+    against each group's largest |O|), and the LSE is untouched."""
+    w = configs.MXFP4_RAGGED.scaled(B=2, Hq=hq, ctx_range=(3000, 9000), P=4)
+    inp = synth.make_inputs(w, 77, device=DEV, needles=True)
+    gen = torch.Generator().manual_seed(5)
+    shift = torch.randint(-60, 31, tuple(inp.v_scale.shape), generator=gen, dtype=torch.int16)
+    inp.v_scale = (inp.v_scale.cpu().to(torch.int16) + shift).clamp(1, 254).to(torch.uint8).to(DEV)
+    H.log(f"[mxfp4 wide exponents] G={w.G} ctx={inp.ctx}")
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    oc, lc = o.cpu().numpy(), lse.cpu().numpy()
+    for b, g in H.all_groups(inp):
+        _, _, O, L = H.oracle_group(inp, b, g)
+        cols = g * w.G + np.arange(w.G)
+        rel = float(np.max(np.abs(oc[b, cols] - O)) / np.max(np.abs(O)))
+        lrel = float(np.max(np.abs(lc[b, cols] - L) / np.maximum(1.0, np.abs(L))))
+        H.log(f"   b={b} g={g} max|O|={np.max(np.abs(O)):.2e} |dO|/max|O|={rel:.2e} LSE rel={lrel:.2e}")
+        assert np.all(np.isfinite(oc[b, cols]))
+        assert rel <= H.TOL["mxfp4"]["rel_o"] and lrel <= H.LSE_REL
+
+
 # ---------------------------------------------------------------- attention parity
 
 PARITY_CASES = [
