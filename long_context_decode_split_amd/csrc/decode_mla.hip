@@ -318,29 +318,38 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       const lds_u8* st = (const lds_u8*)&s_stage[k & 1][0];
       lds_u8* dt = (lds_u8*)&s_tile[k % kNB][0];
       const int valid = min(kTileTok, ntok - k * kTileTok);
-      constexpr int kItems = kTileTok * (kDk / 8);   // 2,304
+      // Thread t converts row t / 8, pieces q0 + 8 j (q0 = t % 8, j = 0 .. 8):
+      // the row, its swizzle and its chunk are the thread's own, so a piece's
+      // source and destination are the thread's bases plus 8 j pieces (the
+      // swizzle permutes within groups of 8, so piece q0 + 8 j lands at
+      // (q0 ^ swizzle) + 8 j).  A wave's eight rows and eight pieces per row
+      // read 64 different LDS banks (MXFP4) or two rows per bank group (fp8).
+      constexpr int kCodeRow = FMT == 1 ? kDk : kDk / 2;   // code bytes per row
+      const int m = threadIdx.x >> 3, q0 = threadIdx.x & 7;
+      const lds_u8* src = st + (m >> 4) * kQChunk<FMT> + (m & 15) * kCodeRow + (FMT == 1 ? 8 : 4) * q0;
+      const lds_u8* esrc = st + (m >> 4) * kQChunk<FMT> + kQCodes<FMT> + (m & 15) * (kDk / 32) + (q0 >> 2);
+      lds_u8* dst = dt + m * kRowBytes + 16 * (q0 ^ mla_swz(m));
+      const bool live = m < valid;
       // one piece at a time: the accumulators and Q fragments leave few registers
 #pragma unroll 1
-      for (int j = 0; j < kItems / kThreads; ++j) {
-        const int i = threadIdx.x + kThreads * j;
-        const int m = i / (kDk / 8), q = i - m * (kDk / 8);
-        const lds_u8* cb = st + (m >> 4) * kQChunk<FMT>;   // the row's chunk tile
-        const int mr = m & 15;
+      for (int j = 0; j < kDk / 64; ++j) {
         uint4 out = make_uint4(0u, 0u, 0u, 0u);
-        if (m < valid) {
+        if (live) {
           if constexpr (FMT == 1) {
-            const uint2 c8 = *(const __attribute__((address_space(3))) uint2*)(cb + mr * kDk + 8 * q);
+            const uint2 c8 = *(const __attribute__((address_space(3))) uint2*)src;
             out = make_uint4(frag::fp8x2_to_bf16x2<false>(c8.x), frag::fp8x2_to_bf16x2<true>(c8.x),
                              frag::fp8x2_to_bf16x2<false>(c8.y), frag::fp8x2_to_bf16x2<true>(c8.y));
           } else {
-            const uint32_t c4 = *(const __attribute__((address_space(3))) uint32_t*)(cb + mr * (kDk / 2) + 4 * q);
-            const uint32_t e = cb[kQCodes<FMT> + mr * (kDk / 32) + (q >> 2)];
-            const float sc = __uint_as_float(e << 23);   // 2^(E-127); E = 0 reads as 0, E = 255 as +inf
+            const uint32_t c4 = *(const __attribute__((address_space(3))) uint32_t*)src;
+            const float sc = __uint_as_float((uint32_t)*esrc << 23);   // 2^(E-127); E = 0 reads as 0, E = 255 as +inf
             out = make_uint4(frag::fp4x2_to_bf16x2<0>(c4, sc), frag::fp4x2_to_bf16x2<1>(c4, sc),
                              frag::fp4x2_to_bf16x2<2>(c4, sc), frag::fp4x2_to_bf16x2<3>(c4, sc));
           }
         }
-        *(lds_u4*)(dt + m * kRowBytes + 16 * (q ^ mla_swz(m))) = out;
+        *(lds_u4*)dst = out;
+        src += FMT == 1 ? 64 : 32;
+        esrc += 2;
+        dst += 128;
       }
       if constexpr (FMT == 1) {   // a group with no row of the slice: scale 1 (its rows are zeros)
         if (threadIdx.x < 2)
