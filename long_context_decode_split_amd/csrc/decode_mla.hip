@@ -170,6 +170,13 @@ __device__ __forceinline__ int opaque_lane() {
   return l;
 }
 
+// The same for the thread index.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
@@ -297,12 +304,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
         c1p = valid > kChunk ? c0p + a.k_tile : c0p;
       }
       uint8_t* dst = &s_stage[k & 1][0];
-      const int pbeg = 2 * N * wave / kWaves, pend = 2 * N * (wave + 1) / kWaves;
+      // the wave index as a scalar, so the piece range and the LDS
+      // destinations are scalar values too (as vector values they were
+      // spilled to scratch and reloaded behind a wait for every load)
+      const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int pbeg = 2 * N * wv / kWaves, pend = 2 * N * (wv + 1) / kWaves;
+      // dense cache: both chunk tiles within 4 GiB of the first, so one
+      // scalar base and 32-bit lane offsets (recomputed here from the lane,
+      // not kept live across the loop as per-lane 64-bit addresses)
+      const uint32_t gap = (uint32_t)(c1p - c0p) - 16u * N;   // the second chunk's offset past piece N
 #pragma unroll
       for (int i = 0; i < kQCopies<FMT>; ++i) {
         const int first = pbeg + 64 * i;
-        const int pc = first + lane;
-        if (pc < pend) dma16a(pc < N ? c0p + 16 * pc : c1p + 16 * (pc - N), lds_addr(dst + 16 * first));
+        const int pc = first + (PAGED ? lane : opaque_lane());
+        if (pc < pend) {
+          if constexpr (PAGED) dma16a(pc < N ? c0p + 16 * pc : c1p + 16 * (pc - N), lds_addr(dst + 16 * first));
+          else dma16(16u * pc + (pc < N ? 0u : gap), c0p, lds_addr(dst + 16 * first));
+        }
       }
     }
   };
@@ -313,51 +331,90 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
   //      in s_qscale for the softmax, which folds them into the scores and
   //      into P; MXFP4: e2m1 x 2^(E-127), exact in bf16.  Each thread
   //      converts 9 of the tile's 32 x 72 pieces of 8 elements.
+  //      The work is split into reads and conversions of three pieces at a
+  //      time (cvt_load, cvt_store) so that it can run as one phase (all
+  //      reads first: the LDS round trips overlap) or between the products.
+  struct CvtAt {
+    const lds_u8* src;    // the thread's first code piece in the staging buffer
+    const lds_u8* esrc;   // MXFP4: its first e8m0 byte
+    lds_u8* dst;          // its first piece in the bf16 buffer
+    bool live;            // the thread's row holds a token of the slice
+  };
+  auto cvt_at = [&](int k) {
+    // Thread t converts row t / 8, pieces q0 + 8 j (q0 = t % 8, j = 0 .. 8):
+    // the row, its swizzle and its chunk are the thread's own, so a piece's
+    // source and destination are the thread's bases plus 8 j pieces (the
+    // swizzle permutes within groups of 8, so piece q0 + 8 j lands at
+    // (q0 ^ swizzle) + 8 j).  A wave's eight rows and eight pieces per row
+    // read 64 different LDS banks (MXFP4) or two rows per bank group (fp8).
+    constexpr int kCodeRow = FMT == 1 ? kDk : kDk / 2;   // code bytes per row
+    const lds_u8* st = (const lds_u8*)&s_stage[k & 1][0];
+    const int t = opaque_tid();
+    const int m = t >> 3, q0 = t & 7;
+    CvtAt c;
+    c.src = st + (m >> 4) * kQChunk<FMT> + (m & 15) * kCodeRow + (FMT == 1 ? 8 : 4) * q0;
+    c.esrc = st + (m >> 4) * kQChunk<FMT> + kQCodes<FMT> + (m & 15) * (kDk / 32) + (q0 >> 2);
+    c.dst = (lds_u8*)&s_tile[k % kNB][0] + m * kRowBytes + 16 * (q0 ^ mla_swz(m));
+    c.live = m < min(kTileTok, ntok - k * kTileTok);
+    return c;
+  };
+  struct CvtRegs {
+    uint32_t q[3][FMT == 1 ? 2 : 1];   // codes of three pieces
+    uint32_t e[3];                     // MXFP4: their e8m0 bytes
+  };
+  auto cvt_load = [&](const CvtAt& c, int j0, CvtRegs& r) {   // reads of pieces j0 .. j0 + 2 (in the staging buffer either way)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if constexpr (FMT == 1) {
+        const uint2 c8 = *(const __attribute__((address_space(3))) uint2*)(c.src + 64 * (j0 + i));
+        r.q[i][0] = c8.x;
+        r.q[i][1] = c8.y;
+      } else if constexpr (FMT == 2) {
+        r.q[i][0] = *(const __attribute__((address_space(3))) uint32_t*)(c.src + 32 * (j0 + i));
+        r.e[i] = c.esrc[2 * (j0 + i)];
+      }
+    }
+  };
+  auto cvt_store = [&](const CvtAt& c, int j0, const CvtRegs& r) {   // conversions and stores of pieces j0 .. j0 + 2
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      uint4 out = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (FMT == 1) {
+        out = make_uint4(frag::fp8x2_to_bf16x2<false>(r.q[i][0]), frag::fp8x2_to_bf16x2<true>(r.q[i][0]),
+                         frag::fp8x2_to_bf16x2<false>(r.q[i][1]), frag::fp8x2_to_bf16x2<true>(r.q[i][1]));
+      } else if constexpr (FMT == 2) {
+        const float sc = __uint_as_float(r.e[i] << 23);   // 2^(E-127); E = 0 reads as 0, E = 255 as +inf
+        out = make_uint4(frag::fp4x2_to_bf16x2<0>(r.q[i][0], sc), frag::fp4x2_to_bf16x2<1>(r.q[i][0], sc),
+                         frag::fp4x2_to_bf16x2<2>(r.q[i][0], sc), frag::fp4x2_to_bf16x2<3>(r.q[i][0], sc));
+      }
+      if (!c.live) out = make_uint4(0u, 0u, 0u, 0u);   // rows past the slice end: zeros
+      *(lds_u4*)(c.dst + 128 * (j0 + i)) = out;
+    }
+  };
+  // fp8: the two group scales of tile k for the softmax (a group with no row
+  // of the slice: scale 1, its rows being zeros)
+  auto cvt_scales = [&](int k) {
+    if constexpr (FMT == 1) {
+      const lds_u8* st = (const lds_u8*)&s_stage[k & 1][0];
+      const int valid = min(kTileTok, ntok - k * kTileTok);
+      const int t = opaque_tid();
+      if (t < 2)
+        s_qscale[k % kNB][t] =
+            16 * t < valid ? *(const __attribute__((address_space(3))) float*)(st + t * kQChunk<FMT> + kQCodes<FMT>)
+                           : 1.0f;
+    }
+  };
+  // the whole conversion of tile k as one phase: all nine reads, then the
+  // conversions (one piece at a time waited for nine round trips in a row)
   auto convert = [&](int k) {
     if constexpr (FMT != 0) {
-      const lds_u8* st = (const lds_u8*)&s_stage[k & 1][0];
-      lds_u8* dt = (lds_u8*)&s_tile[k % kNB][0];
-      const int valid = min(kTileTok, ntok - k * kTileTok);
-      // Thread t converts row t / 8, pieces q0 + 8 j (q0 = t % 8, j = 0 .. 8):
-      // the row, its swizzle and its chunk are the thread's own, so a piece's
-      // source and destination are the thread's bases plus 8 j pieces (the
-      // swizzle permutes within groups of 8, so piece q0 + 8 j lands at
-      // (q0 ^ swizzle) + 8 j).  A wave's eight rows and eight pieces per row
-      // read 64 different LDS banks (MXFP4) or two rows per bank group (fp8).
-      constexpr int kCodeRow = FMT == 1 ? kDk : kDk / 2;   // code bytes per row
-      const int m = threadIdx.x >> 3, q0 = threadIdx.x & 7;
-      const lds_u8* src = st + (m >> 4) * kQChunk<FMT> + (m & 15) * kCodeRow + (FMT == 1 ? 8 : 4) * q0;
-      const lds_u8* esrc = st + (m >> 4) * kQChunk<FMT> + kQCodes<FMT> + (m & 15) * (kDk / 32) + (q0 >> 2);
-      lds_u8* dst = dt + m * kRowBytes + 16 * (q0 ^ mla_swz(m));
-      const bool live = m < valid;
-      // one piece at a time: the accumulators and Q fragments leave few registers
-#pragma unroll 1
-      for (int j = 0; j < kDk / 64; ++j) {
-        uint4 out = make_uint4(0u, 0u, 0u, 0u);
-        if (live) {
-          if constexpr (FMT == 1) {
-            const uint2 c8 = *(const __attribute__((address_space(3))) uint2*)src;
-            out = make_uint4(frag::fp8x2_to_bf16x2<false>(c8.x), frag::fp8x2_to_bf16x2<true>(c8.x),
-                             frag::fp8x2_to_bf16x2<false>(c8.y), frag::fp8x2_to_bf16x2<true>(c8.y));
-          } else {
-            const uint32_t c4 = *(const __attribute__((address_space(3))) uint32_t*)src;
-            const float sc = __uint_as_float((uint32_t)*esrc << 23);   // 2^(E-127); E = 0 reads as 0, E = 255 as +inf
-            out = make_uint4(frag::fp4x2_to_bf16x2<0>(c4, sc), frag::fp4x2_to_bf16x2<1>(c4, sc),
-                             frag::fp4x2_to_bf16x2<2>(c4, sc), frag::fp4x2_to_bf16x2<3>(c4, sc));
-          }
-        }
-        *(lds_u4*)dst = out;
-        src += FMT == 1 ? 64 : 32;
-        esrc += 2;
-        dst += 128;
-      }
-      if constexpr (FMT == 1) {   // a group with no row of the slice: scale 1 (its rows are zeros)
-        if (threadIdx.x < 2)
-          s_qscale[k % kNB][threadIdx.x] =
-              16 * (int)threadIdx.x < valid
-                  ? *(const __attribute__((address_space(3))) float*)(st + threadIdx.x * kQChunk<FMT> + kQCodes<FMT>)
-                  : 1.0f;
-      }
+      const CvtAt c = cvt_at(k);
+      CvtRegs r[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) cvt_load(c, 3 * j, r[j]);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) cvt_store(c, 3 * j, r[j]);
+      cvt_scales(k);
     }
   };
 
@@ -525,8 +582,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       if (CUR && k + 3 < ntiles) load_tile(k + 3);
     } else {
       if (k + 3 < ntiles) stage(k + 3);    // into the staging buffer tile k + 1 left
-      if (k + 2 < ntiles) convert(k + 2);  // into the bf16 buffer tile k - 1 left
+      cvt_scales(k + 2);
     }
+    // quantised rows: tile k + 2 is converted into the bf16 buffer tile k - 1
+    // left in three parts between the products below (past the last tile it
+    // converts zeros into a buffer no tile uses any more)
+    CvtAt cv;
+    CvtRegs cr;
+    if constexpr (FMT != 0) cv = cvt_at(k + 2);
     const lds_u8* tv = (const lds_u8*)&s_tile[(k + kNB) % kNB][0];
     const lds_u8* tk = (const lds_u8*)&s_tile[(k + 1) % kNB][0];
     f32x16 sc;
@@ -542,6 +605,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
+      if constexpr (FMT != 0) {
+        if (s % 12 == 0) cvt_load(cv, s / 4, cr);
+        if (s % 12 == 4) cvt_store(cv, (s - 4) / 4, cr);
+      }
       if (CUR && s < 2 * kVBlocks) {
         if (s + 2 < 2 * kVBlocks) vv[(s + 2) % 3] = vread(tv, s + 2);
         const int u = s >> 4;
