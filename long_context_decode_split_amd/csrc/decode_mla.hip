@@ -638,7 +638,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       }
     }
     if (NEXT) {
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");   // the last score step has drained
+      // the last score step has drained; sc is an operand, so the compiler
+      // schedules no read of it before these wait states
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
       softmax(sc, k + 1);
     }
     return false;
