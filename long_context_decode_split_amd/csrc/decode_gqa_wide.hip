@@ -347,14 +347,17 @@ __global__ __launch_bounds__(64 * W, NHW > 1 ? 2 : 1) void gqa_wide_kernel(const
         const int off = FMT == 0 ? 8192 + t * 4096 + p * 1024 : (FMT == 1 ? 4096 + t * 2048 + p * 1024 : t * 2048 + 1024);
         vr[t][p] = *(const lds_u4*)(pb + off + lane * 16);
       }
-    // rows of each tile this lane's V halves may use (tokens 4h+{0,1}, 4h+{2,3})
+    // rows of each tile this lane's V halves may use (tokens 4h+{0,1}, 4h+{2,3});
+    // bf16 and fp8 pairs need no mask here: the V values of rows past the
+    // slice end were zeroed in LDS (zero_tail_v), so their weight 0 adds 0
     uint32_t keep01[2], keep23[2];
     {
       const int vv[2] = {v0, v1};
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        keep01[t] = FULL ? ~0u : (4 * h + 0 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 1 < vv[t] ? 0xffff0000u : 0u);
-        keep23[t] = FULL ? ~0u : (4 * h + 2 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 3 < vv[t] ? 0xffff0000u : 0u);
+        const bool all = FULL || FMT != 2;
+        keep01[t] = all ? ~0u : (4 * h + 0 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 1 < vv[t] ? 0xffff0000u : 0u);
+        keep23[t] = all ? ~0u : (4 * h + 2 < vv[t] ? 0x0000ffffu : 0u) | (4 * h + 3 < vv[t] ? 0xffff0000u : 0u);
       }
     }
 
@@ -371,7 +374,9 @@ __global__ __launch_bounds__(64 * W, NHW > 1 ? 2 : 1) void gqa_wide_kernel(const
 #pragma unroll
         for (int j = 0; j < 4; ++j) s8[4 * t + j] = FMT == 1 ? sc[j] * (c2 * ks[t]) : sc[j];
       }
-      if constexpr (!FULL) {
+      // masked scores: selects, taken only on pairs with rows past the slice
+      // end (a uniform branch: no per-pair cost on full pairs)
+      if (!FULL && (v0 < kChunk || v1 < kChunk)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (4 * h + j >= v0) s8[j] = -INFINITY;
@@ -514,6 +519,43 @@ __global__ __launch_bounds__(64 * W, NHW > 1 ? 2 : 1) void gqa_wide_kernel(const
     }
   };
 
+  // ---- bf16 and fp8 pairs with rows past the slice end (a slice's last
+  //      tile, or the empty second slot of a one-tile pair): the V values of
+  //      those rows, whose bytes may be anything (NaN included), are set to
+  //      zero in the LDS copy once, so the value products need no per-pair
+  //      mask (their weights are 0; 0 times a NaN would not be).  Each 16-byte
+  //      piece of a V tile holds tokens 4h .. 4h + 3 (h = bits 4-5 of the
+  //      piece's lane index) of two value columns (bf16: 2 bytes per token in
+  //      each 8-byte half) or four (fp8: one byte per token in each word).
+  //      Every wave's stores are done before the barrier that follows.
+  auto zero_tail_v = [&](uint8_t* pbw, int v0, int v1) {
+    if constexpr (FMT != 2) {
+      constexpr int kPieces = FMT == 0 ? 256 : 128;   // 16-byte pieces per V tile
+      constexpr int kVOff = FMT == 0 ? 8192 : 4096, kVTile = FMT == 0 ? 4096 : 2048;
+      for (int pi = threadIdx.x; pi < 2 * kPieces; pi += 64 * W) {
+        const int t = pi / kPieces, q = pi % kPieces;
+        const int v = t ? v1 : v0;
+        const int hh = (q & 63) >> 4;
+        if (4 * hh + 3 < v) continue;   // every token of the piece is a row of the slice
+        uint32_t m01, m23;
+        if constexpr (FMT == 0) {
+          m01 = (4 * hh + 0 < v ? 0x0000ffffu : 0u) | (4 * hh + 1 < v ? 0xffff0000u : 0u);
+          m23 = (4 * hh + 2 < v ? 0x0000ffffu : 0u) | (4 * hh + 3 < v ? 0xffff0000u : 0u);
+        } else {
+          m01 = (4 * hh + 0 < v ? 0x000000ffu : 0u) | (4 * hh + 1 < v ? 0x0000ff00u : 0u) |
+                (4 * hh + 2 < v ? 0x00ff0000u : 0u) | (4 * hh + 3 < v ? 0xff000000u : 0u);
+          m23 = m01;
+        }
+        lds_u4* ptr = (lds_u4*)(pbw + kVOff + t * kVTile + 16 * q);
+        uint4 u = *ptr;
+        if constexpr (FMT == 0) u = make_uint4(u.x & m01, u.y & m23, u.z & m01, u.w & m23);
+        else u = make_uint4(u.x & m01, u.y & m01, u.z & m01, u.w & m01);
+        *ptr = u;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
   // ---- the pairs, kNBuf - 1 in flight: pair k lands in buffer k % kNBuf;
   //      iteration k waits for its own copies of pair k, then the barrier
   //      publishes every wave's part and certifies that all waves are done
@@ -538,6 +580,7 @@ __global__ __launch_bounds__(64 * W, NHW > 1 ? 2 : 1) void gqa_wide_kernel(const
       else
         compute(std::false_type{}, pb, v0, v1);
     } else {
+      if (v0 < kChunk || v1 < kChunk) zero_tail_v((uint8_t*)&s_buf[k % kNBuf][0], v0, v1);   // uniform
       compute(std::false_type{}, pb, v0, v1);
     }
   }
