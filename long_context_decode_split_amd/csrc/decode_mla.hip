@@ -577,7 +577,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       if (k + 3 < ntiles) prep(k + 3);
       wait_barrier<0>();
     }
-    if ((s_over[par][0] | s_over[par][1] | s_over[par][2] | s_over[par][3]) != 0) return true;
+    // a restart asked for by some wave.  Quantised rows act on it at the end
+    // of the iteration (its work is then discarded), so the flags' LDS round
+    // trip does not hold up the iteration (the copy issued below lands before
+    // the restart's first barrier; a wave reads these flags before the
+    // barrier of the next iteration, and the next write to them is two
+    // barriers on): MXFP4 rows 2,236-2,258 -> 2,188-2,198 us on one box; bf16
+    // rows, bound by the board's power, measured no gain and return at once.
+    const bool stop = (s_over[par][0] | s_over[par][1] | s_over[par][2] | s_over[par][3]) != 0;
+    if (FMT == 0 && stop) return true;
     if constexpr (FMT == 0) {
       if (CUR && k + 3 < ntiles) load_tile(k + 3);
     } else {
@@ -643,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
       softmax(sc, k + 1);
     }
-    return false;
+    return stop;
   };
   typedef std::integral_constant<bool, true> T;
   typedef std::integral_constant<bool, false> F;
