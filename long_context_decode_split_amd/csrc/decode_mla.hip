@@ -500,14 +500,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
     mseen = fmaxf(mseen, cm);
     if (mref == -INFINITY) mref = cm;   // first tile of the run (at least one valid token)
     float p[16];
-    float ps = 0.f, pm = 0.f;
+    float psg[2] = {0.f, 0.f}, pm = 0.f;   // sums of P over rows 0-15 and 16-31
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -mref));
-      ps += p[i];
+      psg[i >> 3] += p[i];
       pm = fmaxf(pm, p[i]);
     }
-    lsum += ps;
+    lsum += psg[0] + psg[1];
     // the lane's running sum covers half of its head's tokens so far, so the
     // two lanes' sum bounds the head's final sum from below
     if constexpr (SPLITP) res = __any(pm > kResFrac * sum_xor32(lsum));
@@ -517,15 +517,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_partial_kernel(const PartialA
       // unrounded, the values being 0)
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp) {
-        float rs = 0.f, ps2 = 0.f;
+        float rs = 0.f;
 #pragma unroll
         for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
           const bf16x2 pb2 = {(__bf16)(p[2 * i] * gs[grp]), (__bf16)(p[2 * i + 1] * gs[grp])};
           pk[i] = __builtin_bit_cast(uint32_t, pb2);
           rs = __builtin_amdgcn_fdot2_f32_bf16(pb2, kOnes2, rs, false);
-          ps2 += p[2 * i] + p[2 * i + 1];
         }
-        lsum_mfma += gs[grp] != 0.f ? rs / gs[grp] : ps2;
+        // (the hardware reciprocal: a normalising sum needs no correctly
+        // rounded quotient)
+        lsum_mfma += gs[grp] != 0.f ? rs * __builtin_amdgcn_rcpf(gs[grp]) : psg[grp];
       }
     } else {
 #pragma unroll
