@@ -175,3 +175,24 @@ def test_mla_quantised_score_jumps_restart(dtype):
     torch.cuda.synchronize()
     worst = H.check_step(inp, o_part, lse_part, o, lse, label=f"mla {dtype} jumps")
     H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
+
+
+def test_mla_fp8_zero_group_scales():
+    """A zero group scale is a valid fp8 encoding (all values 0): such a
+    group's scores are 0 and its rows add weight but no value, so the kernel
+    normalises by their unrounded weights.  Zero scales in a full group
+    inside a slice and in the partial last group of every request, against
+    the oracle on the dequantised values."""
+    w = configs.DEEPSEEK_MLA.scaled(B=3, ctx=None, ctx_range=(300, 3000), P=4, dtype="fp8_e4m3")
+    inp = synth.make_inputs(w, 73, device=DEV, needles=True)
+    for b, n in enumerate(inp.ctx):
+        last = (n - 1) // 16 * 16                 # first token of the last group
+        inp.k_scale[b, :, last:n] = 0.0
+        inp.k_scale[b, :, 160:176] = 0.0          # and one full group inside a slice
+    H.log(f"[mla fp8 zero scales] ctx={inp.ctx}")
+    cache = H.build_cache(inp)
+    o_part, lse_part, _ = H.run_partials(inp, cache)
+    o, lse = H.run_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    worst = H.check_step(inp, o_part, lse_part, o, lse, label="mla fp8 zero scales")
+    H.log(f"   worst |dO|={worst[0]:.2e} LSE rel={worst[1]:.2e}")
