@@ -55,6 +55,8 @@ CASES = [
     (configs.DEEPSEEK_MLA, True, "ends"),
     (configs.DEEPSEEK_MLA_FP8, True, "ends"),
     (configs.DEEPSEEK_MLA_MXFP4, True, "ends"),
+    # 64 query heads per KV head: the wide-group kernel, all heads checked
+    (configs.WIDE_GQA_G64, True, "ends"),
 ]
 
 # MLA groups hold 128 query heads: the oracle checks heads at both ends of
@@ -82,7 +84,7 @@ def test_full_size_sampled_groups(w, needles, sample):
 
 
 STEP_CASES = [configs.LLAMA405B_SHARE, configs.FP8_GQA, configs.MXFP4_RAGGED, RAGGED_BF16, configs.DEEPSEEK_MLA,
-              configs.DEEPSEEK_MLA_MXFP4]
+              configs.DEEPSEEK_MLA_MXFP4, configs.WIDE_GQA_G64]
 
 
 @pytest.mark.parametrize("w", STEP_CASES, ids=lambda x: x.name)
